@@ -1,0 +1,314 @@
+// C-ABI entry points of libstreamkl: argument validation, workspace sizing and
+// kernel dispatch.  Every check runs on the host before anything is enqueued.
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/streamkl.h"
+#include "skl_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+skl_status fail(skl_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+skl_status ok() {
+  g_last_error.clear();
+  return SKL_OK;
+}
+
+skl_status from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(SKL_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+size_t esize(int dtype) { return dtype == SKL_BF16 ? 2 : 4; }
+
+// Shape checks shared by every call.  `need_nk` is false for skl_reduce.
+skl_status check_shape(const skl_shape* s, bool need_nk) {
+  if (!s) return fail(SKL_ERR_INVALID_ARGUMENT, "shape is NULL");
+  if (s->B < 0 || s->H < 0 || s->NQ < 0 || s->NK < 0)
+    return fail(SKL_ERR_INVALID_ARGUMENT, "negative size (B=%lld H=%lld NQ=%lld NK=%lld)", (long long)s->B,
+                (long long)s->H, (long long)s->NQ, (long long)s->NK);
+  if (s->reserved != 0) return fail(SKL_ERR_INVALID_ARGUMENT, "skl_shape.reserved must be 0");
+  if (s->dtype != SKL_BF16 && s->dtype != SKL_F32) return fail(SKL_ERR_UNSUPPORTED, "dtype %d", s->dtype);
+  if (!need_nk) return ok();
+  if ((s->d1 != 64 && s->d1 != 128) || (s->d2 != 64 && s->d2 != 128))
+    return fail(SKL_ERR_UNSUPPORTED, "head dims d1=%d d2=%d (supported: 64, 128)", s->d1, s->d2);
+  if (s->NK == 0 && s->NQ > 0 && s->B > 0 && s->H > 0)
+    return fail(SKL_ERR_INVALID_ARGUMENT, "N_K = 0 with N_Q > 0: empty softmax");
+  // Index arithmetic inside the kernels: grid sizes fit in 32 bits.
+  if (s->NQ > (int64_t(1) << 31) || s->NK > (int64_t(1) << 31) || s->B * s->H > (int64_t(1) << 31))
+    return fail(SKL_ERR_UNSUPPORTED, "sizes too large");
+  const int64_t mult = s->dtype == SKL_BF16 ? 8 : 4;
+  const int64_t* all[4] = {s->sq1, s->sk1, s->sq2, s->sk2};
+  for (int t = 0; t < 4; ++t)
+    for (int a = 0; a < 3; ++a) {
+      if (all[t][a] < 0) return fail(SKL_ERR_INVALID_ARGUMENT, "negative stride");
+      if (all[t][a] % mult != 0)
+        return fail(SKL_ERR_UNSUPPORTED, "stride %lld not a multiple of %lld elements", (long long)all[t][a],
+                    (long long)mult);
+    }
+  return ok();
+}
+
+bool empty(const skl_shape* s) { return s->B == 0 || s->H == 0 || s->NQ == 0; }
+
+skl_status check_ptr(const void* p, const char* name, bool align16 = true) {
+  if (!p) return fail(SKL_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+  if (align16 && (reinterpret_cast<uintptr_t>(p) & 15u) != 0)
+    return fail(SKL_ERR_UNSUPPORTED, "%s is not 16-byte aligned", name);
+  return ok();
+}
+
+skl_status check_scales(float s1, float s2, int causal, const skl_shape* s) {
+  if (!std::isfinite(s1) || !std::isfinite(s2) || !(s1 > 0.f) || !(s2 > 0.f))
+    return fail(SKL_ERR_INVALID_ARGUMENT, "scales must be finite and > 0 (got %g, %g)", (double)s1, (double)s2);
+  if (causal && s->NQ > s->NK)
+    return fail(SKL_ERR_INVALID_ARGUMENT, "causal needs N_Q <= N_K (got %lld > %lld)", (long long)s->NQ,
+                (long long)s->NK);
+  return ok();
+}
+
+#define SKL_TRY(expr)                 \
+  do {                                \
+    skl_status st_ = (expr);          \
+    if (st_ != SKL_OK) return st_;    \
+  } while (0)
+
+skl_status check_inputs(const skl_shape* s, const void* q1, const void* k1, const void* q2, const void* k2,
+                        float scale1, float scale2, int causal) {
+  SKL_TRY(check_shape(s, true));
+  SKL_TRY(check_scales(scale1, scale2, causal, s));
+  if (empty(s)) return ok();
+  SKL_TRY(check_ptr(q1, "q1"));
+  SKL_TRY(check_ptr(k1, "k1"));
+  SKL_TRY(check_ptr(q2, "q2"));
+  SKL_TRY(check_ptr(k2, "k2"));
+  return ok();
+}
+
+skl::Strides strides(const int64_t* a) { return skl::Strides{a[0], a[1], a[2]}; }
+
+skl::FwdParams fwd_params(const skl_shape* s, const void* q1, const void* k1, const void* q2, const void* k2,
+                          float scale1, float scale2) {
+  skl::FwdParams p{};
+  p.q1 = q1;
+  p.k1 = k1;
+  p.q2 = q2;
+  p.k2 = k2;
+  p.sq1 = strides(s->sq1);
+  p.sk1 = strides(s->sk1);
+  p.sq2 = strides(s->sq2);
+  p.sk2 = strides(s->sk2);
+  p.NQ = s->NQ;
+  p.NK = s->NK;
+  p.H = (int32_t)s->H;
+  p.num_qtiles = (int32_t)cdiv(s->NQ, skl::kFwdBQ);
+  p.splits = 1;
+  p.split_len = 0;
+  p.c1 = (float)(scale1 * 1.4426950408889634);
+  p.c2 = (float)(scale2 * 1.4426950408889634);
+  return p;
+}
+
+int64_t split_len_for(int64_t nk, int splits) {
+  return cdiv(cdiv(nk, splits), skl::kFwdBK) * skl::kFwdBK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int skl_version(void) { return 100; }
+
+const char* skl_last_error(void) { return g_last_error.c_str(); }
+
+const char* skl_status_string(skl_status st) {
+  switch (st) {
+    case SKL_OK: return "SKL_OK";
+    case SKL_ERR_INVALID_ARGUMENT: return "SKL_ERR_INVALID_ARGUMENT";
+    case SKL_ERR_UNSUPPORTED: return "SKL_ERR_UNSUPPORTED";
+    case SKL_ERR_WORKSPACE_TOO_SMALL: return "SKL_ERR_WORKSPACE_TOO_SMALL";
+    case SKL_ERR_HIP: return "SKL_ERR_HIP";
+  }
+  return "SKL_UNKNOWN_STATUS";
+}
+
+skl_status skl_forward(const skl_shape* s, const void* q1, const void* k1, const void* q2, const void* k2,
+                       float scale1, float scale2, int causal, float* kl, float* lse1, float* lse2,
+                       hipStream_t stream) {
+  SKL_TRY(check_inputs(s, q1, k1, q2, k2, scale1, scale2, causal));
+  if (empty(s)) return ok();
+  SKL_TRY(check_ptr(kl, "kl", false));
+  SKL_TRY(check_ptr(lse1, "lse1", false));
+  SKL_TRY(check_ptr(lse2, "lse2", false));
+  skl::FwdParams p = fwd_params(s, q1, k1, q2, k2, scale1, scale2);
+  p.kl = kl;
+  p.lse1 = lse1;
+  p.lse2 = lse2;
+  return from_hip(skl::launch_forward(p, s->dtype, s->d1, s->d2, causal != 0, false, s->B * s->H, stream),
+                  "skl_forward launch");
+}
+
+size_t skl_forward_splitk_workspace_size(const skl_shape* s, int num_splits) {
+  if (!s || num_splits < 1 || s->B < 0 || s->H < 0 || s->NQ < 0) return 0;
+  return (size_t)5 * (size_t)s->B * (size_t)s->H * (size_t)num_splits * (size_t)s->NQ * sizeof(float);
+}
+
+skl_status skl_forward_splitk(const skl_shape* s, const void* q1, const void* k1, const void* q2, const void* k2,
+                              float scale1, float scale2, int causal, int num_splits, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+  SKL_TRY(check_inputs(s, q1, k1, q2, k2, scale1, scale2, causal));
+  if (num_splits < 1 || num_splits > 65536) return fail(SKL_ERR_INVALID_ARGUMENT, "num_splits=%d", num_splits);
+  if (empty(s)) return ok();
+  SKL_TRY(check_ptr(ws, "ws"));
+  const size_t need = skl_forward_splitk_workspace_size(s, num_splits);
+  if (ws_bytes < need)
+    return fail(SKL_ERR_WORKSPACE_TOO_SMALL, "split-K workspace %zu < %zu bytes", ws_bytes, need);
+  if ((int64_t)s->B * s->H * cdiv(s->NQ, skl::kFwdBQ) * num_splits > (int64_t(1) << 31) - 1)
+    return fail(SKL_ERR_UNSUPPORTED, "grid too large");
+  skl::FwdParams p = fwd_params(s, q1, k1, q2, k2, scale1, scale2);
+  p.splits = num_splits;
+  p.split_len = (int32_t)split_len_for(s->NK, num_splits);
+  p.part = static_cast<float*>(ws);
+  return from_hip(skl::launch_forward(p, s->dtype, s->d1, s->d2, causal != 0, true, s->B * s->H, stream),
+                  "skl_forward_splitk launch");
+}
+
+skl_status skl_reduce(const skl_shape* s, int num_splits, const void* ws, size_t ws_bytes, float* kl, float* lse1,
+                      float* lse2, hipStream_t stream) {
+  SKL_TRY(check_shape(s, false));
+  if (num_splits < 1 || num_splits > 65536) return fail(SKL_ERR_INVALID_ARGUMENT, "num_splits=%d", num_splits);
+  if (empty(s)) return ok();
+  SKL_TRY(check_ptr(ws, "ws"));
+  SKL_TRY(check_ptr(kl, "kl", false));
+  SKL_TRY(check_ptr(lse1, "lse1", false));
+  SKL_TRY(check_ptr(lse2, "lse2", false));
+  const size_t need = skl_forward_splitk_workspace_size(s, num_splits);
+  if (ws_bytes < need)
+    return fail(SKL_ERR_WORKSPACE_TOO_SMALL, "split-K workspace %zu < %zu bytes", ws_bytes, need);
+  skl::ReduceParams p{};
+  p.part = static_cast<const float*>(ws);
+  p.rows = s->B * s->H * s->NQ;
+  p.NQ = s->NQ;
+  p.splits = num_splits;
+  p.kl = kl;
+  p.lse1 = lse1;
+  p.lse2 = lse2;
+  return from_hip(skl::launch_reduce(p, stream), "skl_reduce launch");
+}
+
+size_t skl_backward_workspace_size(const skl_shape* s, int teacher) {
+  if (!s || s->B < 0 || s->H < 0 || s->NQ < 0) return 0;
+  const int d = teacher ? s->d1 : s->d2;
+  if (d <= 0) return 0;
+  return (size_t)s->B * (size_t)s->H * (size_t)s->NQ * (size_t)d * sizeof(float);
+}
+
+static skl_status backward_common(const skl_shape* s, const void* q1, const void* k1, const void* q2,
+                                  const void* k2, float scale1, float scale2, int causal, const float* lse1,
+                                  const float* lse2, const float* kl, const float* dkl, void* dq, void* dk,
+                                  void* ws, size_t ws_bytes, bool teacher, hipStream_t stream) {
+  SKL_TRY(check_inputs(s, q1, k1, q2, k2, scale1, scale2, causal));
+  if (empty(s)) return ok();
+  SKL_TRY(check_ptr(lse1, "lse1", false));
+  SKL_TRY(check_ptr(lse2, "lse2", false));
+  if (teacher) SKL_TRY(check_ptr(kl, "kl", false));
+  SKL_TRY(check_ptr(dkl, "dkl", false));
+  SKL_TRY(check_ptr(dq, teacher ? "dq1" : "dq2"));
+  SKL_TRY(check_ptr(dk, teacher ? "dk1" : "dk2"));
+  SKL_TRY(check_ptr(ws, "ws"));
+  const size_t need = skl_backward_workspace_size(s, teacher ? 1 : 0);
+  if (ws_bytes < need)
+    return fail(SKL_ERR_WORKSPACE_TOO_SMALL, "backward workspace %zu < %zu bytes", ws_bytes, need);
+  const int64_t BH = s->B * s->H;
+  const int dg = teacher ? s->d1 : s->d2;
+  const float scale_g = teacher ? scale1 : scale2;
+
+  hipError_t e = skl::launch_zero(static_cast<float*>(ws), BH * s->NQ * dg, stream);
+  if (e != hipSuccess) return from_hip(e, "workspace clear launch");
+
+  skl::BwdParams p{};
+  p.q1 = q1;
+  p.k1 = k1;
+  p.q2 = q2;
+  p.k2 = k2;
+  p.sq1 = strides(s->sq1);
+  p.sk1 = strides(s->sk1);
+  p.sq2 = strides(s->sq2);
+  p.sk2 = strides(s->sk2);
+  p.NQ = s->NQ;
+  p.NK = s->NK;
+  p.H = (int32_t)s->H;
+  p.num_ktiles = (int32_t)cdiv(s->NK, skl::kBwdBK);
+  p.c1 = (float)(scale1 * 1.4426950408889634);
+  p.c2 = (float)(scale2 * 1.4426950408889634);
+  p.scale_g = scale_g;
+  p.lse1 = lse1;
+  p.lse2 = lse2;
+  p.kl = kl;
+  p.dkl = dkl;
+  p.dk = dk;
+  p.sdk = teacher ? p.sk1 : p.sk2;
+  p.ws = static_cast<float*>(ws);
+  e = skl::launch_backward(p, s->dtype, s->d1, s->d2, causal != 0, teacher, BH, stream);
+  if (e != hipSuccess) return from_hip(e, "backward launch");
+
+  skl::ConvertParams c{};
+  c.ws = static_cast<const float*>(ws);
+  c.dq = dq;
+  c.sdq = teacher ? p.sq1 : p.sq2;
+  c.NQ = s->NQ;
+  c.H = (int32_t)s->H;
+  c.dg = dg;
+  c.rows = BH * s->NQ;
+  c.scale = scale_g;
+  return from_hip(skl::launch_convert(c, s->dtype, stream), "dq convert launch");
+}
+
+skl_status skl_backward_student(const skl_shape* s, const void* q1, const void* k1, const void* q2, const void* k2,
+                                float scale1, float scale2, int causal, const float* lse1, const float* lse2,
+                                const float* dkl, void* dq2, void* dk2, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  return backward_common(s, q1, k1, q2, k2, scale1, scale2, causal, lse1, lse2, nullptr, dkl, dq2, dk2, ws,
+                         ws_bytes, false, stream);
+}
+
+skl_status skl_backward_teacher(const skl_shape* s, const void* q1, const void* k1, const void* q2, const void* k2,
+                                float scale1, float scale2, int causal, const float* lse1, const float* lse2,
+                                const float* kl, const float* dkl, void* dq1, void* dk1, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  return backward_common(s, q1, k1, q2, k2, scale1, scale2, causal, lse1, lse2, kl, dkl, dq1, dk1, ws, ws_bytes,
+                         true, stream);
+}
+
+int skl_recommended_splits(const skl_shape* s, int causal, int num_cus) {
+  if (!s || s->B <= 0 || s->H <= 0 || s->NQ <= 0 || s->NK <= 0 || num_cus <= 0) return 1;
+  // Two resident forward workgroups per CU; aim for at least two waves of them.
+  const int64_t target = 4 * (int64_t)num_cus;
+  const int64_t tiles = s->B * s->H * cdiv(s->NQ, skl::kFwdBQ);
+  if (tiles >= target) return 1;
+  // Each split keeps at least 4 key tiles of work (for causal, of the longest rows).
+  const int64_t max_by_keys = cdiv(s->NK, 4 * skl::kFwdBK);
+  int64_t splits = cdiv(target, tiles);
+  if (splits > max_by_keys) splits = max_by_keys;
+  if (splits > 64) splits = 64;
+  (void)causal;
+  return (int)(splits < 1 ? 1 : splits);
+}
+
+}  // extern "C"

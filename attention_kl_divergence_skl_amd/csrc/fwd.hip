@@ -1,0 +1,287 @@
+// Forward kernels of the fused attention-KL primitive for gfx950.
+//
+// One workgroup = 4 waves = 128 query rows of one (b, h).  It streams the key
+// tiles of K1 and K2 through LDS once and, per tile, forms both logit tiles on
+// MFMA and updates per-row online statistics (agidaily.cc StreamKL article,
+// sections "Online formula" and "Forward: single-pass streaming kernel"):
+//
+//   m_k  running max of t_k = S_k * log2(e)         (base-2 logits)
+//   l_k  running sum of 2^(t_k - m_k)
+//   acc  running sum of 2^(t_1 - m_1) * (t_1 - t_2)   (rescaled with m_1 only)
+//
+// and finishes with KL = ln2 * acc / l1 + LSE2 - LSE1, LSE_k = ln2 (m_k + log2 l_k).
+// Only acc, a per-row scalar, needs the correction factor: the logit difference
+// is not rescaled by anything, so no d-wide output is rescaled.
+//
+// Layout on chip.  Each wave computes S^T = K Q^T for its 32 queries: the
+// query is the MFMA column (lane % 32), so each lane owns one query row and 16
+// keys of every 32-key block.  Row reductions are then in-lane; the two lane
+// halves hold disjoint key subsets of the same row and run their own online
+// statistics, merged once at the end.  Q fragments stay in registers for the
+// whole key loop; K tiles are staged in LDS (padded rows, conflict-free 16-byte
+// reads) and shared by the 4 waves.
+//
+// Split-K (article section "GPU kernel optimisations"): the same kernel over a
+// contiguous key range writes the five per-row partials (m1, l1, m2, l2, acc)
+// instead of the final values; reduce_kernel merges them.
+
+#include "skl_device.h"
+#include "skl_internal.h"
+
+namespace skl {
+
+template <typename T, int D1, int D2, bool CAUSAL, bool SPLIT>
+__global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const FwdParams p) {
+  using M = Mfma<T>;
+  using frag = typename M::frag;
+  constexpr int KC = M::KC, EPL = M::EPL;
+  constexpr int NC1 = D1 / KC, NC2 = D2 / KC;
+  constexpr int ESZ = sizeof(T);
+  constexpr int PITCH1 = D1 * ESZ + 16;  // LDS row pitch in bytes (16-byte pad)
+  constexpr int PITCH2 = D2 * ESZ + 16;
+  constexpr int CPR1 = D1 * ESZ / 16;    // 16-byte chunks per key row
+  constexpr int CPR2 = D2 * ESZ / 16;
+  __shared__ __attribute__((aligned(16))) char smem[kFwdBK * (PITCH1 + PITCH2)];
+  char* const sk1 = smem;
+  char* const sk2 = smem + kFwdBK * PITCH1;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, col = lane & 31;
+
+  // Tile decode: logical tile -> (bh, query tile[, split]).
+  int64_t t = xcd_remap(blockIdx.x, gridDim.x);
+  int split = 0;
+  if (SPLIT) {
+    split = (int)(t % p.splits);
+    t /= p.splits;
+  }
+  const int64_t bh = t / p.num_qtiles;
+  int qt = (int)(t % p.num_qtiles);
+  if (CAUSAL) qt = p.num_qtiles - 1 - qt;  // longest rows first
+  const int64_t b = bh / p.H, h = bh % p.H;
+  const int64_t off = p.NK - p.NQ;
+
+  const int64_t qw0 = (int64_t)qt * kFwdBQ + wave * 32;  // first query of this wave
+  const int64_t qi = qw0 + col;                           // this lane's query
+  const bool qvalid = qi < p.NQ;
+
+  const char* const q1p = (const char*)p.q1 + (b * p.sq1.b + h * p.sq1.h) * ESZ;
+  const char* const q2p = (const char*)p.q2 + (b * p.sq2.b + h * p.sq2.h) * ESZ;
+  const char* const k1p = (const char*)p.k1 + (b * p.sk1.b + h * p.sk1.h) * ESZ;
+  const char* const k2p = (const char*)p.k2 + (b * p.sk2.b + h * p.sk2.h) * ESZ;
+
+  // Q fragments (MFMA B operand: column = query, K slot = head-dim index).
+  frag qf1[NC1], qf2[NC2];
+#pragma unroll
+  for (int c = 0; c < NC1; ++c)
+    qf1[c] = qvalid ? M::load(q1p + (qi * p.sq1.n + c * KC + half * EPL) * ESZ) : M::zero();
+#pragma unroll
+  for (int c = 0; c < NC2; ++c)
+    qf2[c] = qvalid ? M::load(q2p + (qi * p.sq2.n + c * KC + half * EPL) * ESZ) : M::zero();
+
+  // Key range of this workgroup.
+  int64_t kbeg = 0, kend = p.NK;
+  if (CAUSAL) kend = min(kend, (int64_t)(qt + 1) * kFwdBQ + off);
+  if (SPLIT) {
+    kbeg = (int64_t)split * p.split_len;
+    kend = min(kend, kbeg + (int64_t)p.split_len);
+  }
+  const int64_t wave_kmax = CAUSAL ? qw0 + 31 + off : p.NK - 1;  // last key any row of the wave sees
+
+  const float c1 = p.c1, c2 = p.c2;
+  float m1 = neg_inf(), m2 = neg_inf(), l1 = 0.f, l2 = 0.f, acc = 0.f;
+
+  for (int64_t j0 = kbeg; j0 < kend; j0 += kFwdBK) {
+    __syncthreads();  // previous tile fully consumed
+    for (int idx = tid; idx < kFwdBK * CPR1; idx += kThreads) {
+      const int row = idx / CPR1, ch = idx % CPR1;
+      const int64_t key = j0 + row;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (key < p.NK) v = ld16(k1p + key * p.sk1.n * ESZ + ch * 16);
+      st16(sk1 + row * PITCH1 + ch * 16, v);
+    }
+    for (int idx = tid; idx < kFwdBK * CPR2; idx += kThreads) {
+      const int row = idx / CPR2, ch = idx % CPR2;
+      const int64_t key = j0 + row;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (key < p.NK) v = ld16(k2p + key * p.sk2.n * ESZ + ch * 16);
+      st16(sk2 + row * PITCH2 + ch * 16, v);
+    }
+    __syncthreads();
+    if (j0 > wave_kmax) continue;  // the whole tile is masked for this wave
+
+    f32x16 s1[2], s2[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s1[kb] = f32x16{};
+      s2[kb] = f32x16{};
+      const char* a1 = sk1 + (kb * 32 + col) * PITCH1 + half * EPL * ESZ;
+      const char* a2 = sk2 + (kb * 32 + col) * PITCH2 + half * EPL * ESZ;
+#pragma unroll
+      for (int c = 0; c < NC1; ++c) s1[kb] = M::run(M::load(a1 + c * KC * ESZ), qf1[c], s1[kb]);
+#pragma unroll
+      for (int c = 0; c < NC2; ++c) s2[kb] = M::run(M::load(a2 + c * KC * ESZ), qf2[c], s2[kb]);
+    }
+
+    const bool need_mask = (j0 + kFwdBK > p.NK) || (CAUSAL && j0 + kFwdBK - 1 > qw0 + off);
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t key = j0 + kb * 32 + acc_row(r, half);
+          const bool ok = key < p.NK && (!CAUSAL || key <= qi + off);
+          if (!ok) {
+            s1[kb][r] = neg_inf();
+            s2[kb][r] = neg_inf();
+          }
+        }
+    }
+
+    float mx1 = neg_inf(), mx2 = neg_inf();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        mx1 = fmaxf(mx1, s1[kb][r]);
+        mx2 = fmaxf(mx2, s2[kb][r]);
+      }
+    const float m1n = fmaxf(m1, mx1 * c1), m2n = fmaxf(m2, mx2 * c2);
+    const float m1u = (m1n == neg_inf()) ? 0.f : m1n;  // no key seen yet: keep sums at 0
+    const float m2u = (m2n == neg_inf()) ? 0.f : m2n;
+    const float a1 = exp2_hw(m1 - m1u), a2 = exp2_hw(m2 - m2u);
+
+    float sum1 = 0.f, sum2 = 0.f, accd = 0.f;
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float u1 = fmaf(s1[kb][r], c1, -m1u), u2 = fmaf(s2[kb][r], c2, -m2u);
+          const float e1 = exp2_hw(u1), e2 = exp2_hw(u2);
+          sum1 += e1;
+          sum2 += e2;
+          const float d = (s1[kb][r] == neg_inf()) ? 0.f : (u1 - u2);
+          accd = fmaf(e1, d, accd);
+        }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float u1 = fmaf(s1[kb][r], c1, -m1u), u2 = fmaf(s2[kb][r], c2, -m2u);
+          const float e1 = exp2_hw(u1), e2 = exp2_hw(u2);
+          sum1 += e1;
+          sum2 += e2;
+          accd = fmaf(e1, u1 - u2, accd);
+        }
+    }
+    // t1 - t2 = (u1 - u2) + (m1u - m2u): the per-row part is added once per tile.
+    l1 = fmaf(l1, a1, sum1);
+    l2 = fmaf(l2, a2, sum2);
+    acc = fmaf(acc, a1, fmaf(m1u - m2u, sum1, accd));
+    m1 = m1n;
+    m2 = m2n;
+  }
+
+  // Merge the two lane halves (disjoint key subsets of the same row).
+  const float om1 = __shfl_xor(m1, 32), ol1 = __shfl_xor(l1, 32);
+  const float om2 = __shfl_xor(m2, 32), ol2 = __shfl_xor(l2, 32);
+  const float oacc = __shfl_xor(acc, 32);
+  const float M1 = fmaxf(m1, om1), M2 = fmaxf(m2, om2);
+  const float M1u = (M1 == neg_inf()) ? 0.f : M1;
+  const float M2u = (M2 == neg_inf()) ? 0.f : M2;
+  const float wa1 = exp2_hw(m1 - M1u), wb1 = exp2_hw(om1 - M1u);
+  const float wa2 = exp2_hw(m2 - M2u), wb2 = exp2_hw(om2 - M2u);
+  const float L1 = l1 * wa1 + ol1 * wb1;
+  const float L2 = l2 * wa2 + ol2 * wb2;
+  const float ACC = acc * wa1 + oacc * wb1;
+
+  if (half == 0 && qvalid) {
+    if (SPLIT) {
+      const int64_t BH = gridDim.x / ((int64_t)p.num_qtiles * p.splits);
+      const int64_t stride_f = BH * p.splits * p.NQ;
+      float* dst = p.part + (bh * p.splits + split) * p.NQ + qi;
+      dst[0] = M1;
+      dst[stride_f] = L1;
+      dst[2 * stride_f] = M2;
+      dst[3 * stride_f] = L2;
+      dst[4 * stride_f] = ACC;
+    } else {
+      const float lg1 = log2f(L1), lg2 = log2f(L2);
+      const int64_t o = bh * p.NQ + qi;
+      p.lse1[o] = kLn2 * (M1 + lg1);
+      p.lse2[o] = kLn2 * (M2 + lg2);
+      p.kl[o] = kLn2 * (ACC / L1 + (M2 - M1) + (lg2 - lg1));
+    }
+  }
+}
+
+// Merge split-K partials: one thread per row.
+__global__ __launch_bounds__(256) void reduce_kernel(const ReduceParams p) {
+  const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (row >= p.rows) return;
+  const int64_t bh = row / p.NQ, i = row % p.NQ;
+  const int64_t stride_f = p.rows * p.splits;
+  const float* src = p.part + bh * p.splits * p.NQ + i;
+  float M1 = neg_inf(), M2 = neg_inf();
+  for (int s = 0; s < p.splits; ++s) {
+    M1 = fmaxf(M1, src[s * p.NQ]);
+    M2 = fmaxf(M2, src[2 * stride_f + s * p.NQ]);
+  }
+  const float M1u = (M1 == neg_inf()) ? 0.f : M1;
+  const float M2u = (M2 == neg_inf()) ? 0.f : M2;
+  float L1 = 0.f, L2 = 0.f, ACC = 0.f;
+  for (int s = 0; s < p.splits; ++s) {
+    const float w1 = exp2_hw(src[s * p.NQ] - M1u);
+    const float w2 = exp2_hw(src[2 * stride_f + s * p.NQ] - M2u);
+    L1 = fmaf(src[stride_f + s * p.NQ], w1, L1);
+    ACC = fmaf(src[4 * stride_f + s * p.NQ], w1, ACC);
+    L2 = fmaf(src[3 * stride_f + s * p.NQ], w2, L2);
+  }
+  const float lg1 = log2f(L1), lg2 = log2f(L2);
+  p.lse1[row] = kLn2 * (M1 + lg1);
+  p.lse2[row] = kLn2 * (M2 + lg2);
+  p.kl[row] = kLn2 * (ACC / L1 + (M2 - M1) + (lg2 - lg1));
+}
+
+namespace {
+
+template <typename T, int D1, int D2, bool C, bool S>
+hipError_t run_fwd(const FwdParams& p, int64_t BH, hipStream_t s) {
+  const int64_t grid = BH * p.num_qtiles * (S ? p.splits : 1);
+  hipLaunchKernelGGL((fwd_kernel<T, D1, D2, C, S>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+template <typename T, int D1, int D2>
+hipError_t fwd_dims(const FwdParams& p, bool causal, bool split, int64_t BH, hipStream_t s) {
+  if (causal) return split ? run_fwd<T, D1, D2, true, true>(p, BH, s) : run_fwd<T, D1, D2, true, false>(p, BH, s);
+  return split ? run_fwd<T, D1, D2, false, true>(p, BH, s) : run_fwd<T, D1, D2, false, false>(p, BH, s);
+}
+
+template <typename T>
+hipError_t fwd_type(const FwdParams& p, int d1, int d2, bool causal, bool split, int64_t BH, hipStream_t s) {
+  if (d1 == 128 && d2 == 128) return fwd_dims<T, 128, 128>(p, causal, split, BH, s);
+  if (d1 == 128 && d2 == 64) return fwd_dims<T, 128, 64>(p, causal, split, BH, s);
+  if (d1 == 64 && d2 == 128) return fwd_dims<T, 64, 128>(p, causal, split, BH, s);
+  if (d1 == 64 && d2 == 64) return fwd_dims<T, 64, 64>(p, causal, split, BH, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_forward(const FwdParams& p, int dtype, int d1, int d2, bool causal, bool split,
+                          int64_t BH, hipStream_t s) {
+  if (dtype == 0) return fwd_type<bf16>(p, d1, d2, causal, split, BH, s);
+  return fwd_type<float>(p, d1, d2, causal, split, BH, s);
+}
+
+hipError_t launch_reduce(const ReduceParams& p, hipStream_t s) {
+  const int64_t blocks = (p.rows + 255) / 256;
+  hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace skl

@@ -1,0 +1,81 @@
+// Device-side helpers shared by the gfx950 kernels: element types, MFMA
+// wrappers, fragment loads and base-2 exponentials.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace skl {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+// v_exp_f32: 2^x on the transcendental unit (no libm wrapper).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// One 32x32 MFMA step, D = A*B + C with fp32 accumulation.
+//  * bf16: v_mfma_f32_32x32x16_bf16, K = 16, each lane holds 8 K-values.
+//  * fp32: v_mfma_f32_32x32x2_f32,   K = 2,  each lane holds 1 K-value.
+// Operand layout (both types): lane l supplies A[i = l % 32][kslot(l / 32)]
+// and B[kslot(l / 32)][j = l % 32]; the accumulator register r of lane l is
+// D[8 * (r / 4) + 4 * (l / 32) + r % 4][l % 32].  Which K index each
+// (lane half, element) slot carries does not matter as long as A and B agree.
+template <typename T>
+struct Mfma;
+
+template <>
+struct Mfma<bf16> {
+  typedef bf16x8 frag;
+  static constexpr int KC = 16;   // K per instruction
+  static constexpr int EPL = 8;   // K-values per lane
+  __device__ __forceinline__ static f32x16 run(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static frag load(const void* p) { return *reinterpret_cast<const frag*>(p); }
+  __device__ __forceinline__ static frag zero() { return frag{}; }
+};
+
+template <>
+struct Mfma<float> {
+  typedef float frag;
+  static constexpr int KC = 2;
+  static constexpr int EPL = 1;
+  __device__ __forceinline__ static f32x16 run(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static frag load(const void* p) { return *reinterpret_cast<const float*>(p); }
+  __device__ __forceinline__ static frag zero() { return 0.0f; }
+};
+
+// Row of the 32x32 accumulator held in register r by a lane of half `half`.
+__device__ __forceinline__ int acc_row(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }
+
+// 16-byte copy global -> LDS through registers.
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // RNE (v_cvt_pk_bf16_f32)
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+
+// Map a linear workgroup id so that consecutive logical tiles land on the same
+// XCD: the hardware hands workgroup i to XCD i % 8, so logical tile
+// x * (G / 8) + k is given to workgroup 8 * k + x.  Tiles of one head then run
+// together on one XCD and share its L2.
+__device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t grid) {
+  constexpr int kXcds = 8;
+  if (grid % kXcds != 0) return bid;
+  return (bid % kXcds) * (grid / kXcds) + bid / kXcds;
+}
+
+}  // namespace skl

@@ -1,0 +1,89 @@
+// Internal interface between the C-ABI host code (api.cpp) and the kernel
+// translation units.  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace skl {
+
+// Geometry fixed by the kernels.
+constexpr int kFwdBQ = 128;  // queries per forward workgroup (4 waves x 32)
+constexpr int kFwdBK = 64;   // keys per forward pipeline step
+constexpr int kBwdBK = 128;  // keys per backward workgroup (4 waves x 32)
+constexpr int kBwdBQ = 32;   // queries per backward step
+constexpr int kThreads = 256;
+
+struct Strides {
+  int64_t b, h, n;
+};
+
+struct FwdParams {
+  const void* q1;
+  const void* k1;
+  const void* q2;
+  const void* k2;
+  Strides sq1, sk1, sq2, sk2;
+  int64_t NQ, NK;
+  int32_t H;
+  int32_t num_qtiles;   // ceil(NQ / kFwdBQ)
+  int32_t splits;       // 1 for the plain forward
+  int32_t split_len;    // keys per split (multiple of kFwdBK); unused when splits == 1
+  float c1, c2;         // scale_k * log2(e)
+  float* kl;            // plain forward outputs [B*H*NQ]
+  float* lse1;
+  float* lse2;
+  float* part;          // split-K partials: [5][B*H][splits][NQ]
+};
+
+struct ReduceParams {
+  const float* part;
+  int64_t rows;         // B*H*NQ
+  int64_t NQ;
+  int32_t splits;
+  float* kl;
+  float* lse1;
+  float* lse2;
+};
+
+struct BwdParams {
+  const void* q1;
+  const void* k1;
+  const void* q2;
+  const void* k2;
+  Strides sq1, sk1, sq2, sk2;
+  int64_t NQ, NK;
+  int32_t H;
+  int32_t num_ktiles;   // ceil(NK / kBwdBK)
+  float c1, c2;         // scale_k * log2(e)
+  float scale_g;        // scale of the optimised side
+  const float* lse1;
+  const float* lse2;
+  const float* kl;      // teacher only
+  const float* dkl;
+  void* dk;             // gradient of the optimised side's keys (input strides)
+  Strides sdk;
+  float* ws;            // fp32 dQ accumulator [B*H][NQ][dg]
+};
+
+struct ConvertParams {
+  const float* ws;
+  void* dq;
+  Strides sdq;
+  int64_t NQ;
+  int32_t H;
+  int32_t dg;
+  int64_t rows;         // B*H*NQ
+  float scale;
+};
+
+// Launchers: return the result of hipGetLastError() after the launch.
+hipError_t launch_forward(const FwdParams& p, int dtype, int d1, int d2, bool causal, bool split,
+                          int64_t BH, hipStream_t s);
+hipError_t launch_reduce(const ReduceParams& p, hipStream_t s);
+hipError_t launch_zero(float* ws, int64_t count, hipStream_t s);
+hipError_t launch_backward(const BwdParams& p, int dtype, int d1, int d2, bool causal, bool teacher,
+                           int64_t BH, hipStream_t s);
+hipError_t launch_convert(const ConvertParams& p, int dtype, hipStream_t s);
+
+}  // namespace skl

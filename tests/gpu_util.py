@@ -1,0 +1,94 @@
+"""Helpers shared by the GPU parity tests: run the HIP path on a synth
+workload and compare with the float64 oracle under the stated tolerances.
+
+Tolerances (per-row KL and LSE, gradients as relative L2 per tensor and per head):
+  fp32 inputs: |dKL| <= 1e-5 |KL_ref| (+1e-7 abs when KL_ref is exactly 0),
+               |dLSE| <= 1e-5, gradients <= 1e-4;
+  bf16 inputs: |dKL| <= 2e-3 + 1e-2 |KL_ref|, |dLSE| <= 1e-3, gradients <= 1e-2.
+"""
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from attention_kl_divergence_skl_amd import synth
+
+TOL = {
+    "f32": dict(kl_rel=1e-5, kl_abs=1e-7, lse=1e-5, grad=1e-4),
+    "bf16": dict(kl_rel=1e-2, kl_abs=2e-3, lse=1e-3, grad=1e-2),
+}
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_device(w: synth.Workload, layout: str = "bhnd"):
+    """All heads of a small workload: (numpy inputs dict, torch tensors dict)."""
+    x = synth.all_inputs(w)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    t = {}
+    for k in ("q1", "k1", "q2", "k2"):
+        a = torch.from_numpy(np.ascontiguousarray(x[k])).to(tdt)
+        if layout == "bnhd":
+            a = a.transpose(1, 2).contiguous().transpose(1, 2)
+        t[k] = a.cuda()
+    t["g"] = torch.from_numpy(x["g"]).cuda()
+    return x, t
+
+
+def check_rows(name, w, got, ref, rows=None):
+    """Compare per-row kl, lse1, lse2 (numpy float64 refs) with GPU values."""
+    tol = TOL[w.dtype]
+    kl_g = got["kl"].astype(np.float64)
+    kl_r = ref["kl"]
+    assert np.all(np.isfinite(kl_g)), f"{name}: non-finite KL"
+    bound = tol["kl_abs"] + tol["kl_rel"] * np.abs(kl_r) if w.dtype == "bf16" else \
+        np.maximum(tol["kl_rel"] * np.abs(kl_r), np.where(kl_r == 0, tol["kl_abs"], 0.0))
+    err = np.abs(kl_g - kl_r)
+    bad = err > bound
+    assert not bad.any(), (f"{name}: KL off in {bad.sum()} rows; worst err {err.max():.3e} "
+                           f"at {np.unravel_index(err.argmax(), err.shape)}")
+    for k in ("lse1", "lse2"):
+        e = np.abs(got[k].astype(np.float64) - ref[k])
+        assert e.max() <= tol["lse"], f"{name}: {k} max err {e.max():.3e}"
+
+
+def rel_l2(a, b) -> float:
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def check_grad(name, w, got, ref, per_head_axis=True):
+    tol = TOL[w.dtype]["grad"]
+    got = np.asarray(got, np.float64)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite gradient"
+    e = rel_l2(got, ref)
+    assert e <= tol, f"{name}: relative L2 error {e:.3e} > {tol}"
+    if per_head_axis and got.ndim == 4:
+        for b in range(got.shape[0]):
+            for h in range(got.shape[1]):
+                if np.linalg.norm(ref[b, h]) > 0:
+                    eh = rel_l2(got[b, h], ref[b, h])
+                    assert eh <= tol, f"{name}: head ({b},{h}) relative L2 {eh:.3e} > {tol}"
+
+
+def gpu_forward(skl, w, t):
+    kl, l1, l2 = skl.skl_forward(t["q1"], t["k1"], t["q2"], t["k2"], w.scale1, w.scale2, w.causal)
+    torch.cuda.synchronize()
+    return {"kl": kl.cpu().numpy(), "lse1": l1.cpu().numpy(), "lse2": l2.cpu().numpy()}, (kl, l1, l2)
+
+
+def oracle_forward(w, x):
+    return oracle.forward(x["q1"], x["k1"], x["q2"], x["k2"], w.scale1, w.scale2, w.causal)
+
+
+def oracle_backward(w, x, setting):
+    return oracle.backward(x["q1"], x["k1"], x["q2"], x["k2"], w.scale1, w.scale2, w.causal, x["g"], setting)
+
+
+def grad_to_np(t):
+    return t.float().cpu().numpy()
