@@ -21,7 +21,7 @@ __all__ = [
     "load", "SklError", "skl_forward", "skl_forward_splitk", "skl_reduce",
     "skl_backward_student", "skl_backward_teacher", "skl_recommended_splits",
     "skl_forward_splitk_workspace_size", "skl_backward_workspace_size",
-    "skl_version", "LIB_PATH",
+    "skl_version", "skl_set_kernel_events", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libstreamkl.so")
@@ -66,6 +66,7 @@ _SIGS = {
     "skl_status_string": (ctypes.c_char_p, [_I]),
     "skl_last_error": (ctypes.c_char_p, []),
     "skl_version": (_I, []),
+    "skl_set_kernel_events": (_I, [_P, _P]),
 }
 
 
@@ -94,6 +95,19 @@ def _check(status: int) -> None:
 
 def skl_version() -> int:
     return load().skl_version()
+
+
+def skl_set_kernel_events(start=None, stop=None) -> None:
+    """Record two torch.cuda.Event objects around the main kernel of every
+    following call on this thread (None, None switches it off).  The events
+    must already exist on the device (record them once first)."""
+    def h(e):
+        if e is None:
+            return None
+        if not e.cuda_event:
+            raise SklError(1, "event not created yet: record it once before passing it")
+        return e.cuda_event
+    _check(load().skl_set_kernel_events(h(start), h(stop)))
 
 
 # ------------------------------------------------------------- marshalling ----

@@ -12,6 +12,20 @@
 namespace {
 
 thread_local std::string g_last_error;
+thread_local hipEvent_t g_ev_start = nullptr;
+thread_local hipEvent_t g_ev_stop = nullptr;
+
+// Record the profiling events (if set) around the main kernel launch.
+template <typename F>
+hipError_t timed(hipStream_t stream, F&& launch) {
+  if (g_ev_start) {
+    hipError_t e = hipEventRecord(g_ev_start, stream);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = launch();
+  if (e == hipSuccess && g_ev_stop) e = hipEventRecord(g_ev_stop, stream);
+  return e;
+}
 
 skl_status fail(skl_status st, const char* fmt, ...) {
   char buf[512];
@@ -135,6 +149,14 @@ extern "C" {
 
 int skl_version(void) { return 100; }
 
+skl_status skl_set_kernel_events(hipEvent_t start, hipEvent_t stop) {
+  if ((start == nullptr) != (stop == nullptr))
+    return fail(SKL_ERR_INVALID_ARGUMENT, "start and stop must both be set or both be NULL");
+  g_ev_start = start;
+  g_ev_stop = stop;
+  return ok();
+}
+
 const char* skl_last_error(void) { return g_last_error.c_str(); }
 
 const char* skl_status_string(skl_status st) {
@@ -160,7 +182,9 @@ skl_status skl_forward(const skl_shape* s, const void* q1, const void* k1, const
   p.kl = kl;
   p.lse1 = lse1;
   p.lse2 = lse2;
-  return from_hip(skl::launch_forward(p, s->dtype, s->d1, s->d2, causal != 0, false, s->B * s->H, stream),
+  return from_hip(timed(stream, [&] {
+                    return skl::launch_forward(p, s->dtype, s->d1, s->d2, causal != 0, false, s->B * s->H, stream);
+                  }),
                   "skl_forward launch");
 }
 
@@ -185,7 +209,9 @@ skl_status skl_forward_splitk(const skl_shape* s, const void* q1, const void* k1
   p.splits = num_splits;
   p.split_len = (int32_t)split_len_for(s->NK, num_splits);
   p.part = static_cast<float*>(ws);
-  return from_hip(skl::launch_forward(p, s->dtype, s->d1, s->d2, causal != 0, true, s->B * s->H, stream),
+  return from_hip(timed(stream, [&] {
+                    return skl::launch_forward(p, s->dtype, s->d1, s->d2, causal != 0, true, s->B * s->H, stream);
+                  }),
                   "skl_forward_splitk launch");
 }
 
@@ -265,7 +291,7 @@ static skl_status backward_common(const skl_shape* s, const void* q1, const void
   p.dk = dk;
   p.sdk = teacher ? p.sk1 : p.sk2;
   p.ws = static_cast<float*>(ws);
-  e = skl::launch_backward(p, s->dtype, s->d1, s->d2, causal != 0, teacher, BH, stream);
+  e = timed(stream, [&] { return skl::launch_backward(p, s->dtype, s->d1, s->d2, causal != 0, teacher, BH, stream); });
   if (e != hipSuccess) return from_hip(e, "backward launch");
 
   skl::ConvertParams c{};

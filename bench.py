@@ -1,0 +1,280 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention-KL hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input
+already resident in HBM: skl_forward (one-pass forward), then
+skl_backward_student (optimise P2) and skl_backward_teacher (optimise P1),
+each with its workspace clear and dQ convert.  W untimed warm-up steps, then
+exactly K timed steps between two device synchronisations.
+
+Prints ONE JSON line.  `value` is the step's algorithmic TFLOP/s
+(2*pairs*[(d1+d2) + (d1+3*d2) + (3*d1+d2)] per step / step time).  The
+`roofline` object describes the kernel that takes the most time per step,
+timed with HIP events recorded by the library itself around that kernel on
+its launch stream; `cpu_baseline` is the float64 CPU oracle timed on a
+bounded causal sub-problem of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fwd/bwd ms & TFLOP/s, causal 64K, H=32, d=128 bf16; % of MFMA peak"
+DEFAULT_WORKLOAD = "causal_64k_h32_d128_q1x4"
+KERNEL_SOURCES = {
+    "fwd": ["fwd.hip", "skl_device.h", "skl_internal.h"],
+    "student": ["bwd.hip", "skl_device.h", "skl_internal.h"],
+    "teacher": ["bwd.hip", "skl_device.h", "skl_internal.h"],
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_sha(kind: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, "attention_kl_divergence_skl_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def kernel_traffic(kind: str, workload: str):
+    """HBM bytes per launch from the committed PMC summary, only if it was
+    taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            data = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    ent = data.get(workload, {}).get(kind)
+    if not ent or ent.get("source_sha") != source_sha(kind):
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, n_sub: int):
+    """Oracle (float64, numpy) on the leading n_sub x n_sub causal block of head
+    (0, 0): forward plus both backward settings; the rate is the same
+    algorithmic flop count the GPU value uses, for that sub-problem."""
+    import numpy as np
+
+    import oracle
+    from attention_kl_divergence_skl_amd import synth, workmodel
+
+    q1, k1, q2, k2 = synth.head_inputs(w.with_(NQ=n_sub, NK=n_sub), 0, 0)
+    g = synth.head_grad(w.with_(NQ=n_sub, NK=n_sub), 0, 0)
+    threads = None
+    try:
+        import threadpoolctl
+
+        threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=None)
+    except Exception:  # noqa: BLE001 - report unknown
+        threads = None
+    args = (q1, k1, q2, k2, w.scale1, w.scale2, w.causal)
+    t0 = time.perf_counter()
+    oracle.head_forward(*args)
+    oracle.head_backward(*args, g, "student")
+    oracle.head_backward(*args, g, "teacher")
+    dt = time.perf_counter() - t0
+    wk = workmodel.work(1, 1, n_sub, n_sub, w.d1, w.d2, w.causal)
+    flops = wk.fwd_flops + wk.student_flops + wk.teacher_flops
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads or len(os.sched_getaffinity(0)),
+        "kind": "oracle",
+        "sample": (f"float64 oracle forward + student + teacher backward on the leading "
+                   f"{n_sub}x{n_sub} {'causal ' if w.causal else ''}block of head (0,0), "
+                   f"{dt:.1f} s wall; host has {os.cpu_count()} cores"),
+        "seconds": dt,
+    }
+
+
+def copy_calibration(nbytes: int, reps: int) -> None:
+    """A plain copy kernel of known size, for scaling HBM byte counters."""
+    import torch
+
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps}), flush=True)
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--phases", default="fwd,student,teacher",
+                    help="comma list of fwd, student, teacher (profiling aid; the default is the full step)")
+    ap.add_argument("--cpu-sub", type=int, default=16384, help="side of the causal block the oracle times")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="MiB",
+                    help="only run a plain copy of this many MiB (counter calibration) and exit")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the attention-KL kernels here run on a single MI355X "
+              "(multi-GPU sharding is a design note, not part of this build); use --gpus 1.",
+              file=sys.stderr, flush=True)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import attention_kl_divergence_skl_amd as skl
+    from attention_kl_divergence_skl_amd import synth, workmodel
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    if args.copy_calib:
+        copy_calibration(args.copy_calib << 20, 5)
+        return 0
+    skl.load()
+
+    w = synth.WORKLOADS[args.workload]
+    phases = [p for p in args.phases.split(",") if p]
+    for p in phases:
+        if p not in ("fwd", "student", "teacher"):
+            raise SystemExit(f"unknown phase {p}")
+    log(f"workload {w.name}: generating inputs")
+    t0 = time.perf_counter()
+    t = synth.device_inputs(w, "cuda")
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
+    q1, k1, q2, k2, g = t["q1"], t["k1"], t["q2"], t["k2"], t["g"]
+    ebytes = 2 if w.dtype == "bf16" else 4
+    wk = workmodel.work(w.B, w.H, w.NQ, w.NK, w.d1, w.d2, w.causal, ebytes)
+
+    # Workspaces are allocated once, outside the timed region.
+    ws_s = torch.empty(skl.skl_backward_workspace_size(q1, k1, q2, k2, False) // 4, dtype=torch.float32,
+                       device="cuda")
+    ws_t = torch.empty(skl.skl_backward_workspace_size(q1, k1, q2, k2, True) // 4, dtype=torch.float32,
+                       device="cuda")
+
+    ev = {p: [] for p in phases}        # main-kernel events
+    pev = {p: [] for p in phases}       # whole-call events
+
+    def step(record: bool):
+        out = {}
+        kl = l1 = l2 = None
+        for p in ("fwd", "student", "teacher"):
+            need = p in phases or (p == "fwd" and phases != ["fwd"])
+            if not need:
+                continue
+            if record and p in phases:
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+                e[0].record()   # torch creates the HIP event on first record;
+                e[1].record()   # the library re-records both around its kernel
+                skl.skl_set_kernel_events(e[0], e[1])
+                e[2].record()
+            if p == "fwd":
+                kl, l1, l2 = skl.skl_forward(q1, k1, q2, k2, w.scale1, w.scale2, w.causal)
+            elif p == "student":
+                out["s"] = skl.skl_backward_student(q1, k1, q2, k2, l1, l2, g, w.scale1, w.scale2, w.causal,
+                                                    ws=ws_s)
+            else:
+                out["t"] = skl.skl_backward_teacher(q1, k1, q2, k2, l1, l2, kl, g, w.scale1, w.scale2,
+                                                    w.causal, ws=ws_t)
+            if record and p in phases:
+                e[3].record()
+                skl.skl_set_kernel_events(None, None)
+                ev[p].append((e[0], e[1]))
+                pev[p].append((e[2], e[3]))
+        return out
+
+    # Extra HBM of one step: peak allocation beyond resident inputs and outputs.
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    o = step(False)
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated() - base
+    out_bytes = 3 * w.B * w.H * w.NQ * 4
+    out_bytes += sum(x.numel() * x.element_size() for v in o.values() for x in v)
+    extra = peak - out_bytes + ws_s.numel() * 4 + ws_t.numel() * 4
+    del o
+
+    for i in range(args.warmup):
+        step(False)
+        torch.cuda.synchronize()
+        log(f"warm-up step {i + 1}/{args.warmup} done")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    log(f"{args.steps} timed steps in {elapsed:.3f} s")
+
+    ms = lambda pairs: float(np.mean([a.elapsed_time(b) for a, b in pairs]))  # noqa: E731
+    flops = {"fwd": wk.fwd_flops, "student": wk.student_flops, "teacher": wk.teacher_flops}
+    peak_tf = workmodel.PEAK_BF16_DENSE_TFLOPS if w.dtype == "bf16" else workmodel.PEAK_FP32_MFMA_TFLOPS
+    kern = {}
+    for p in phases:
+        kms = ms(ev[p])
+        kern[p] = {"kernel_ms": kms, "call_ms": ms(pev[p]), "tflops": flops[p] / (kms * 1e-3) / 1e12}
+        kern[p]["pct_mfma_peak"] = 100.0 * kern[p]["tflops"] / peak_tf
+    step_flops = sum(flops[p] for p in phases)
+    ms_step = elapsed / args.steps * 1e3
+    dom = max(phases, key=lambda p: kern[p]["kernel_ms"])
+    ach = kern[dom]["tflops"]
+    traffic = kernel_traffic(dom, w.name)
+    names = {"fwd": "fwd_kernel", "student": "bwd_kernel (student)", "teacher": "bwd_kernel (teacher)"}
+    res = {
+        "metric": METRIC,
+        "value": step_flops / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N_Q": w.NQ, "N_K": w.NK, "d1": w.d1, "d2": w.d2,
+                   "causal": w.causal, "step": "+".join(phases)},
+        "phases": kern,
+        "extra_hbm_bytes": int(extra),
+        "materialised_bytes": int(wk.materialised_bytes),
+        "roofline": {
+            "kernel": names[dom],
+            "bound": "mfma",
+            "achieved": ach,
+            "peak": peak_tf,
+            "unit": "TFLOP/s",
+            "frac": ach / peak_tf,
+            "traffic": traffic,
+            "algorithmic_flops_per_launch": flops[dom],
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log(f"timing the oracle on a {args.cpu_sub}x{args.cpu_sub} block")
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_sub)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    raise SystemExit(main())

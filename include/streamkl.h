@@ -159,6 +159,16 @@ skl_status skl_backward_teacher(const skl_shape* shape,
  */
 int skl_recommended_splits(const skl_shape* shape, int causal, int num_cus);
 
+/*
+ * Profiling aid.  After this call, every entry point called on this thread
+ * records `start` on its stream immediately before enqueueing its main
+ * kernel (the forward, split-K forward or fused backward kernel; not the
+ * workspace clear, the reduce or the dQ convert) and `stop` right after it,
+ * so hipEventElapsedTime(start, stop) is that kernel's duration.  Pass NULL
+ * for both to switch it off.  The events stay owned by the caller.
+ */
+skl_status skl_set_kernel_events(hipEvent_t start, hipEvent_t stop);
+
 /* Static description of a status code. */
 const char* skl_status_string(skl_status status);
 
