@@ -27,6 +27,8 @@ __all__ = [
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libstreamkl.so")
 
 SKL_BF16, SKL_F32 = 0, 1
+SKL_BWD_SPLIT, SKL_BWD_FUSED_ATOMIC = 0, 1
+_ALGOS = {"split": SKL_BWD_SPLIT, "fused_atomic": SKL_BWD_FUSED_ATOMIC}
 _STATUS = {0: "SKL_OK", 1: "SKL_ERR_INVALID_ARGUMENT", 2: "SKL_ERR_UNSUPPORTED",
            3: "SKL_ERR_WORKSPACE_TOO_SMALL", 4: "SKL_ERR_HIP"}
 
@@ -59,14 +61,14 @@ _SIGS = {
     "skl_forward_splitk_workspace_size": (_SZ, [_SP, _I]),
     "skl_forward_splitk": (_I, [_SP, _P, _P, _P, _P, _F, _F, _I, _I, _P, _SZ, _P]),
     "skl_reduce": (_I, [_SP, _I, _P, _SZ, _P, _P, _P, _P]),
-    "skl_backward_workspace_size": (_SZ, [_SP, _I]),
-    "skl_backward_student": (_I, [_SP, _P, _P, _P, _P, _F, _F, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
-    "skl_backward_teacher": (_I, [_SP, _P, _P, _P, _P, _F, _F, _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "skl_backward_workspace_size": (_SZ, [_SP, _I, _I]),
+    "skl_backward_student": (_I, [_SP, _P, _P, _P, _P, _F, _F, _I, _P, _P, _P, _P, _P, _I, _P, _SZ, _P]),
+    "skl_backward_teacher": (_I, [_SP, _P, _P, _P, _P, _F, _F, _I, _P, _P, _P, _P, _P, _P, _I, _P, _SZ, _P]),
     "skl_recommended_splits": (_I, [_SP, _I, _I]),
     "skl_status_string": (ctypes.c_char_p, [_I]),
     "skl_last_error": (ctypes.c_char_p, []),
     "skl_version": (_I, []),
-    "skl_set_kernel_events": (_I, [_P, _P]),
+    "skl_set_kernel_events": (_I, [ctypes.POINTER(ctypes.c_void_p), _I]),
 }
 
 
@@ -97,17 +99,19 @@ def skl_version() -> int:
     return load().skl_version()
 
 
-def skl_set_kernel_events(start=None, stop=None) -> None:
-    """Record two torch.cuda.Event objects around the main kernel of every
-    following call on this thread (None, None switches it off).  The events
-    must already exist on the device (record them once first)."""
-    def h(e):
-        if e is None:
-            return None
+def skl_set_kernel_events(events=()) -> None:
+    """Have the library record ``events`` (torch.cuda.Event objects, up to 4)
+    around the main kernels of every following call on this thread: events[0]
+    before the first main kernel, events[k] after the k-th.  An empty list
+    switches it off.  Each event must already exist on the device (record it
+    once first)."""
+    handles = []
+    for e in events:
         if not e.cuda_event:
             raise SklError(1, "event not created yet: record it once before passing it")
-        return e.cuda_event
-    _check(load().skl_set_kernel_events(h(start), h(stop)))
+        handles.append(e.cuda_event)
+    arr = (ctypes.c_void_p * max(1, len(handles)))(*handles)
+    _check(load().skl_set_kernel_events(arr, len(handles)))
 
 
 # ------------------------------------------------------------- marshalling ----
@@ -234,9 +238,17 @@ def skl_reduce(ws, num_splits: int, B: int, H: int, NQ: int):
     return tuple(out)
 
 
-def skl_backward_workspace_size(q1, k1, q2, k2, teacher: bool) -> int:
+def _algo(algo) -> int:
+    if isinstance(algo, str):
+        if algo not in _ALGOS:
+            raise SklError(1, f"unknown backward algorithm {algo!r} (split, fused_atomic)")
+        return _ALGOS[algo]
+    return int(algo)
+
+
+def skl_backward_workspace_size(q1, k1, q2, k2, teacher: bool, algo="split") -> int:
     s = make_shape(q1, k1, q2, k2)
-    return int(load().skl_backward_workspace_size(ctypes.byref(s), int(bool(teacher))))
+    return int(load().skl_backward_workspace_size(ctypes.byref(s), int(bool(teacher)), _algo(algo)))
 
 
 def _grad_like(t):
@@ -245,43 +257,47 @@ def _grad_like(t):
     return torch.empty_strided(tuple(t.shape), t.stride(), dtype=t.dtype, device=t.device)
 
 
-def skl_backward_student(q1, k1, q2, k2, lse1, lse2, dkl, scale1=None, scale2=None,
-                         causal: bool = False, ws=None) -> Tuple:
-    """(dq2, dk2) for 'optimise P2'; same dtype and strides as q2, k2."""
+def _ws_for(s, teacher, algo, ws, device):
     import torch
 
+    need = int(load().skl_backward_workspace_size(ctypes.byref(s), int(teacher), algo))
+    if need and ws is None:
+        ws = torch.empty(need // 4, dtype=torch.float32, device=device)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    return ws, nbytes
+
+
+def skl_backward_student(q1, k1, q2, k2, lse1, lse2, dkl, scale1=None, scale2=None,
+                         causal: bool = False, algo="split", ws=None) -> Tuple:
+    """(dq2, dk2) for 'optimise P2'; same dtype and strides as q2, k2."""
     _check_device(q1, k1, q2, k2, lse1, lse2, dkl)
     s = make_shape(q1, k1, q2, k2)
     s1, s2 = _scales(q1, q2, scale1, scale2)
     for t, n in ((lse1, "lse1"), (lse2, "lse2"), (dkl, "dkl")):
         _rowvec(t, s.B, s.H, s.NQ, n)
+    a = _algo(algo)
     dq2, dk2 = _grad_like(q2), _grad_like(k2)
-    need = int(load().skl_backward_workspace_size(ctypes.byref(s), 0))
-    if ws is None:
-        ws = torch.empty(max(need, 4) // 4, dtype=torch.float32, device=q1.device)
+    ws, nbytes = _ws_for(s, 0, a, ws, q1.device)
     _check(load().skl_backward_student(ctypes.byref(s), _ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), s1, s2,
                                        int(causal), _ptr(lse1), _ptr(lse2), _ptr(dkl), _ptr(dq2), _ptr(dk2),
-                                       _ptr(ws), ws.numel() * ws.element_size(), _stream(q1)))
+                                       a, _ptr(ws), nbytes, _stream(q1)))
     return dq2, dk2
 
 
 def skl_backward_teacher(q1, k1, q2, k2, lse1, lse2, kl, dkl, scale1=None, scale2=None,
-                         causal: bool = False, ws=None) -> Tuple:
+                         causal: bool = False, algo="split", ws=None) -> Tuple:
     """(dq1, dk1) for 'optimise P1'; same dtype and strides as q1, k1."""
-    import torch
-
     _check_device(q1, k1, q2, k2, lse1, lse2, kl, dkl)
     s = make_shape(q1, k1, q2, k2)
     s1, s2 = _scales(q1, q2, scale1, scale2)
     for t, n in ((lse1, "lse1"), (lse2, "lse2"), (kl, "kl"), (dkl, "dkl")):
         _rowvec(t, s.B, s.H, s.NQ, n)
+    a = _algo(algo)
     dq1, dk1 = _grad_like(q1), _grad_like(k1)
-    need = int(load().skl_backward_workspace_size(ctypes.byref(s), 1))
-    if ws is None:
-        ws = torch.empty(max(need, 4) // 4, dtype=torch.float32, device=q1.device)
+    ws, nbytes = _ws_for(s, 1, a, ws, q1.device)
     _check(load().skl_backward_teacher(ctypes.byref(s), _ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), s1, s2,
                                        int(causal), _ptr(lse1), _ptr(lse2), _ptr(kl), _ptr(dkl), _ptr(dq1),
-                                       _ptr(dk1), _ptr(ws), ws.numel() * ws.element_size(), _stream(q1)))
+                                       _ptr(dk1), a, _ptr(ws), nbytes, _stream(q1)))
     return dq1, dk1
 
 

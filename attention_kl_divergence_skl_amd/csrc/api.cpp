@@ -12,18 +12,25 @@
 namespace {
 
 thread_local std::string g_last_error;
-thread_local hipEvent_t g_ev_start = nullptr;
-thread_local hipEvent_t g_ev_stop = nullptr;
+// Profiling events (skl_set_kernel_events): slot 0 before the first main
+// kernel of a call, slot k after its k-th main kernel.
+constexpr int kMaxEvents = 4;
+thread_local hipEvent_t g_ev[kMaxEvents] = {};
+thread_local int g_nev = 0;
 
-// Record the profiling events (if set) around the main kernel launch.
+hipError_t mark(int k, hipStream_t s) {
+  if (k < g_nev && g_ev[k]) return hipEventRecord(g_ev[k], s);
+  return hipSuccess;
+}
+void mark1(hipStream_t s) { (void)mark(1, s); }
+
+// Run one main kernel launch between event slots 0 and 1.
 template <typename F>
 hipError_t timed(hipStream_t stream, F&& launch) {
-  if (g_ev_start) {
-    hipError_t e = hipEventRecord(g_ev_start, stream);
-    if (e != hipSuccess) return e;
-  }
-  hipError_t e = launch();
-  if (e == hipSuccess && g_ev_stop) e = hipEventRecord(g_ev_stop, stream);
+  hipError_t e = mark(0, stream);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e == hipSuccess) e = mark(1, stream);
   return e;
 }
 
@@ -149,11 +156,11 @@ extern "C" {
 
 int skl_version(void) { return 100; }
 
-skl_status skl_set_kernel_events(hipEvent_t start, hipEvent_t stop) {
-  if ((start == nullptr) != (stop == nullptr))
-    return fail(SKL_ERR_INVALID_ARGUMENT, "start and stop must both be set or both be NULL");
-  g_ev_start = start;
-  g_ev_stop = stop;
+skl_status skl_set_kernel_events(hipEvent_t* events, int count) {
+  if (count < 0 || count > kMaxEvents || (count > 0 && !events))
+    return fail(SKL_ERR_INVALID_ARGUMENT, "events: count must be 0..%d with a non-NULL array", kMaxEvents);
+  for (int i = 0; i < kMaxEvents; ++i) g_ev[i] = i < count ? events[i] : nullptr;
+  g_nev = count;
   return ok();
 }
 
@@ -238,8 +245,8 @@ skl_status skl_reduce(const skl_shape* s, int num_splits, const void* ws, size_t
   return from_hip(skl::launch_reduce(p, stream), "skl_reduce launch");
 }
 
-size_t skl_backward_workspace_size(const skl_shape* s, int teacher) {
-  if (!s || s->B < 0 || s->H < 0 || s->NQ < 0) return 0;
+size_t skl_backward_workspace_size(const skl_shape* s, int teacher, int algo) {
+  if (!s || s->B < 0 || s->H < 0 || s->NQ < 0 || algo != SKL_BWD_FUSED_ATOMIC) return 0;
   const int d = teacher ? s->d1 : s->d2;
   if (d <= 0) return 0;
   return (size_t)s->B * (size_t)s->H * (size_t)s->NQ * (size_t)d * sizeof(float);
@@ -248,7 +255,7 @@ size_t skl_backward_workspace_size(const skl_shape* s, int teacher) {
 static skl_status backward_common(const skl_shape* s, const void* q1, const void* k1, const void* q2,
                                   const void* k2, float scale1, float scale2, int causal, const float* lse1,
                                   const float* lse2, const float* kl, const float* dkl, void* dq, void* dk,
-                                  void* ws, size_t ws_bytes, bool teacher, hipStream_t stream) {
+                                  int algo, void* ws, size_t ws_bytes, bool teacher, hipStream_t stream) {
   SKL_TRY(check_inputs(s, q1, k1, q2, k2, scale1, scale2, causal));
   if (empty(s)) return ok();
   SKL_TRY(check_ptr(lse1, "lse1", false));
@@ -257,16 +264,18 @@ static skl_status backward_common(const skl_shape* s, const void* q1, const void
   SKL_TRY(check_ptr(dkl, "dkl", false));
   SKL_TRY(check_ptr(dq, teacher ? "dq1" : "dq2"));
   SKL_TRY(check_ptr(dk, teacher ? "dk1" : "dk2"));
-  SKL_TRY(check_ptr(ws, "ws"));
-  const size_t need = skl_backward_workspace_size(s, teacher ? 1 : 0);
-  if (ws_bytes < need)
-    return fail(SKL_ERR_WORKSPACE_TOO_SMALL, "backward workspace %zu < %zu bytes", ws_bytes, need);
+  if (algo != SKL_BWD_SPLIT && algo != SKL_BWD_FUSED_ATOMIC)
+    return fail(SKL_ERR_INVALID_ARGUMENT, "unknown backward algorithm %d", algo);
+  const bool fused = algo == SKL_BWD_FUSED_ATOMIC;
+  if (fused) {
+    SKL_TRY(check_ptr(ws, "ws"));
+    const size_t need = skl_backward_workspace_size(s, teacher ? 1 : 0, algo);
+    if (ws_bytes < need)
+      return fail(SKL_ERR_WORKSPACE_TOO_SMALL, "backward workspace %zu < %zu bytes", ws_bytes, need);
+  }
   const int64_t BH = s->B * s->H;
   const int dg = teacher ? s->d1 : s->d2;
   const float scale_g = teacher ? scale1 : scale2;
-
-  hipError_t e = skl::launch_zero(static_cast<float*>(ws), BH * s->NQ * dg, stream);
-  if (e != hipSuccess) return from_hip(e, "workspace clear launch");
 
   skl::BwdParams p{};
   p.q1 = q1;
@@ -290,8 +299,23 @@ static skl_status backward_common(const skl_shape* s, const void* q1, const void
   p.dkl = dkl;
   p.dk = dk;
   p.sdk = teacher ? p.sk1 : p.sk2;
+  p.dq = dq;
+  p.sdq = teacher ? p.sq1 : p.sq2;
   p.ws = static_cast<float*>(ws);
-  e = timed(stream, [&] { return skl::launch_backward(p, s->dtype, s->d1, s->d2, causal != 0, teacher, BH, stream); });
+
+  if (!fused) {
+    hipError_t e = mark(0, stream);
+    if (e == hipSuccess)
+      e = skl::launch_backward_split(p, s->dtype, s->d1, s->d2, causal != 0, teacher, BH, stream, mark1);
+    if (e == hipSuccess) e = mark(2, stream);
+    return from_hip(e, "backward launch");
+  }
+
+  hipError_t e = skl::launch_zero(static_cast<float*>(ws), BH * s->NQ * dg, stream);
+  if (e != hipSuccess) return from_hip(e, "workspace clear launch");
+  e = timed(stream, [&] {
+    return skl::launch_backward_fused(p, s->dtype, s->d1, s->d2, causal != 0, teacher, BH, stream);
+  });
   if (e != hipSuccess) return from_hip(e, "backward launch");
 
   skl::ConvertParams c{};
@@ -308,18 +332,18 @@ static skl_status backward_common(const skl_shape* s, const void* q1, const void
 
 skl_status skl_backward_student(const skl_shape* s, const void* q1, const void* k1, const void* q2, const void* k2,
                                 float scale1, float scale2, int causal, const float* lse1, const float* lse2,
-                                const float* dkl, void* dq2, void* dk2, void* ws, size_t ws_bytes,
+                                const float* dkl, void* dq2, void* dk2, int algo, void* ws, size_t ws_bytes,
                                 hipStream_t stream) {
-  return backward_common(s, q1, k1, q2, k2, scale1, scale2, causal, lse1, lse2, nullptr, dkl, dq2, dk2, ws,
+  return backward_common(s, q1, k1, q2, k2, scale1, scale2, causal, lse1, lse2, nullptr, dkl, dq2, dk2, algo, ws,
                          ws_bytes, false, stream);
 }
 
 skl_status skl_backward_teacher(const skl_shape* s, const void* q1, const void* k1, const void* q2, const void* k2,
                                 float scale1, float scale2, int causal, const float* lse1, const float* lse2,
-                                const float* kl, const float* dkl, void* dq1, void* dk1, void* ws, size_t ws_bytes,
-                                hipStream_t stream) {
-  return backward_common(s, q1, k1, q2, k2, scale1, scale2, causal, lse1, lse2, kl, dkl, dq1, dk1, ws, ws_bytes,
-                         true, stream);
+                                const float* kl, const float* dkl, void* dq1, void* dk1, int algo, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
+  return backward_common(s, q1, k1, q2, k2, scale1, scale2, causal, lse1, lse2, kl, dkl, dq1, dk1, algo, ws,
+                         ws_bytes, true, stream);
 }
 
 int skl_recommended_splits(const skl_shape* s, int causal, int num_cus) {

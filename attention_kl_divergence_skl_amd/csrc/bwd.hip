@@ -1,4 +1,5 @@
-// Fused backward kernels of the attention-KL primitive for gfx950.
+// Fused backward kernel of the attention-KL primitive for gfx950 (the
+// SKL_BWD_FUSED_ATOMIC algorithm; bwd_split.hip holds the default one).
 //
 // Recompute-based (agidaily.cc StreamKL article, section "Backward:
 // recompute-based tile-by-tile gradients"): P1 = 2^(t1 - LSE1*log2e) and
@@ -20,7 +21,7 @@
 // MFMA orientation.  Each wave computes S = Q K^T for 32 queries x its 32
 // keys; the key is the accumulator column (lane % 32).  The query rows of the
 // A operand are loaded in a permuted order so that accumulator register r of
-// lane half h holds query qloc(r, h) = 16 (r / 8) + 8 h + r % 8: the registers
+// lane half h holds query rloc(r, h) = 16 (r / 8) + 8 h + r % 8: the registers
 // then are directly the A operand of dK += dS^T Q (contraction over queries,
 // 8 consecutive queries per lane).  dQ = dS K contracts over keys, so dS makes
 // one trip through LDS (the only transpose), and K is kept transposed in
@@ -31,14 +32,9 @@
 
 namespace skl {
 
-__device__ __forceinline__ int qloc(int r, int half) { return 16 * (r >> 3) + 8 * half + (r & 7); }
-
-// Query row to load into A-operand row i so that accumulator register r of
-// half h ends up holding qloc(r, h).
-__device__ __forceinline__ int qperm(int i) { return qloc(4 * (i >> 3) + (i & 3), (i >> 2) & 1); }
 
 template <typename T, int D1, int D2, bool CAUSAL, bool TEACHER>
-__global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_kernel(const BwdParams p) {
+__global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_fused_kernel(const BwdParams p) {
   using M = Mfma<T>;
   using frag = typename M::frag;
   constexpr int KC = M::KC, EPL = M::EPL;
@@ -118,7 +114,7 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_kernel(c
   for (int cb = 0; cb < NCB; ++cb) dk[cb] = f32x16{};
 
   const float c1 = p.c1, c2 = p.c2;
-  const int prow = qperm(col);
+  const int prow = rperm(col);
   int64_t qbeg = 0;
   if (CAUSAL) qbeg = max((int64_t)0, kt0 - off) / kBwdBQ * kBwdBQ;
 
@@ -178,7 +174,7 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_kernel(c
                              (CAUSAL && kw0 + 31 > q0 + off);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int ql = qloc(r, half);
+        const int ql = rloc(r, half);
         const float u1 = fmaf(s1[r], c1, -sVec[0][ql]);
         const float u2 = fmaf(s2[r], c2, -sVec[1][ql]);
         const float g = sVec[2][ql];
@@ -206,7 +202,7 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_kernel(c
 #pragma unroll
           for (int e = 0; e < EPL; ++e) a[e] = from_f32<T>(ds[c * EPL + e]);
         }
-        const int qs = (EPL == 1) ? qloc(c, half) : c * KC + half * EPL;
+        const int qs = (EPL == 1) ? rloc(c, half) : c * KC + half * EPL;
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
           const frag bq = M::load(sQT + (32 * cb + col) * PQT + qs * ESZ);
@@ -217,7 +213,7 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_kernel(c
     // dS -> LDS as [query][key] for the dQ contraction over keys.
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      *reinterpret_cast<T*>(sDS + qloc(r, half) * PDS + (32 * wave + col) * ESZ) = from_f32<T>(ds[r]);
+      *reinterpret_cast<T*>(sDS + rloc(r, half) * PDS + (32 * wave + col) * ESZ) = from_f32<T>(ds[r]);
     __syncthreads();
 
     // dQ block (32 queries x 32 columns) over this wave's key part.
@@ -289,7 +285,7 @@ namespace {
 template <typename T, int D1, int D2, bool C, bool TCH>
 hipError_t run_bwd(const BwdParams& p, int64_t BH, hipStream_t s) {
   const int64_t grid = BH * p.num_ktiles;
-  hipLaunchKernelGGL((bwd_kernel<T, D1, D2, C, TCH>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL((bwd_fused_kernel<T, D1, D2, C, TCH>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
@@ -315,8 +311,8 @@ int64_t grid_for(int64_t n, int64_t per_block) {
 
 }  // namespace
 
-hipError_t launch_backward(const BwdParams& p, int dtype, int d1, int d2, bool causal, bool teacher,
-                           int64_t BH, hipStream_t s) {
+hipError_t launch_backward_fused(const BwdParams& p, int dtype, int d1, int d2, bool causal, bool teacher,
+                                 int64_t BH, hipStream_t s) {
   if (dtype == 0) return bwd_type<bf16>(p, d1, d2, causal, teacher, BH, s);
   return bwd_type<float>(p, d1, d2, causal, teacher, BH, s);
 }

@@ -57,6 +57,37 @@ struct Mfma<float> {
 // Row of the 32x32 accumulator held in register r by a lane of half `half`.
 __device__ __forceinline__ int acc_row(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }
 
+// Permuted accumulator rows.  If the A operand's row i is loaded from source
+// row rperm(i), accumulator register r of lane half h holds source row
+// rloc(r, h) = 16 (r / 8) + 8 h + r % 8.  Registers 8c .. 8c+7 of half h then
+// cover 8 consecutive source rows 16c + 8h .. 16c + 8h + 7, which is exactly
+// the K slot layout of the next MFMA's operand: the accumulator can be fed
+// back as an A operand without any data movement.
+__device__ __forceinline__ int rloc(int r, int half) { return 16 * (r >> 3) + 8 * half + (r & 7); }
+__device__ __forceinline__ int rperm(int i) { return rloc(4 * (i >> 3) + (i & 3), (i >> 2) & 1); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Operand of a 32x32x16 bf16 MFMA read from a row-major bf16 tile X in LDS
+// (`pitch` bytes per row) whose rows are the MFMA's K index: lane l receives
+// X[k0 + 8 (l / 32) + e][n0 + l % 32] for e = 0..7.  Uses two gfx950
+// transposing reads (ds_read_b64_tr_b16).  Within each 16-lane group, lane
+// 4j + p reads 4 consecutive elements of row j and the hardware hands element
+// q of lane 4j + p to lane 4p + q as its j-th value.  Addresses are 8-byte
+// aligned when n0 is a multiple of 4 and pitch a multiple of 8.
+__device__ __forceinline__ bf16x8 lds_tr_frag(const char* tile, int pitch, int k0, int n0, int lane) {
+  const int g = lane >> 4, L = lane & 15;
+  const int row = k0 + 8 * (g >> 1) + (L >> 2);
+  const int colx = n0 + 16 * (g & 1) + 4 * (L & 3);
+  const char* a = tile + row * pitch + colx * 2;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a + 4 * pitch));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // 16-byte copy global -> LDS through registers.
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }

@@ -11,7 +11,8 @@ namespace skl {
 constexpr int kFwdBQ = 128;  // queries per forward workgroup (4 waves x 32)
 constexpr int kFwdBK = 64;   // keys per forward pipeline step
 constexpr int kBwdBK = 128;  // keys per backward workgroup (4 waves x 32)
-constexpr int kBwdBQ = 32;   // queries per backward step
+constexpr int kBwdBQ = 32;   // queries per backward step (fused and dK kernels)
+constexpr int kDqBK = 64;    // keys per step of the dQ kernel
 constexpr int kThreads = 256;
 
 struct Strides {
@@ -63,7 +64,9 @@ struct BwdParams {
   const float* dkl;
   void* dk;             // gradient of the optimised side's keys (input strides)
   Strides sdk;
-  float* ws;            // fp32 dQ accumulator [B*H][NQ][dg]
+  void* dq;             // gradient of the optimised side's queries (split kernels)
+  Strides sdq;
+  float* ws;            // fp32 dQ accumulator [B*H][NQ][dg] (fused kernel)
 };
 
 struct ConvertParams {
@@ -82,8 +85,13 @@ hipError_t launch_forward(const FwdParams& p, int dtype, int d1, int d2, bool ca
                           int64_t BH, hipStream_t s);
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s);
 hipError_t launch_zero(float* ws, int64_t count, hipStream_t s);
-hipError_t launch_backward(const BwdParams& p, int dtype, int d1, int d2, bool causal, bool teacher,
-                           int64_t BH, hipStream_t s);
+// Fused backward: one kernel, dQ through fp32 atomics into p.ws.
+hipError_t launch_backward_fused(const BwdParams& p, int dtype, int d1, int d2, bool causal, bool teacher,
+                                 int64_t BH, hipStream_t s);
+// Split backward: dK kernel then dQ kernel, plain stores, no workspace.
+// `between` runs after the first launch (profiling events).
+hipError_t launch_backward_split(const BwdParams& p, int dtype, int d1, int d2, bool causal, bool teacher,
+                                 int64_t BH, hipStream_t s, void (*between)(hipStream_t));
 hipError_t launch_convert(const ConvertParams& p, int dtype, hipStream_t s);
 
 }  // namespace skl

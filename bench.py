@@ -31,37 +31,44 @@ sys.path.insert(0, ROOT)
 METRIC = "fwd/bwd ms & TFLOP/s, causal 64K, H=32, d=128 bf16; % of MFMA peak"
 DEFAULT_WORKLOAD = "causal_64k_h32_d128_q1x4"
 KERNEL_SOURCES = {
-    "fwd": ["fwd.hip", "skl_device.h", "skl_internal.h"],
-    "student": ["bwd.hip", "skl_device.h", "skl_internal.h"],
-    "teacher": ["bwd.hip", "skl_device.h", "skl_internal.h"],
+    "fwd_kernel": ["fwd.hip", "skl_device.h", "skl_internal.h"],
+    "bwd_dk_kernel": ["bwd_split.hip", "skl_device.h", "skl_internal.h"],
+    "bwd_dq_kernel": ["bwd_split.hip", "skl_device.h", "skl_internal.h"],
+    "bwd_fused_kernel": ["bwd.hip", "skl_device.h", "skl_internal.h"],
 }
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.txt")
 
 
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def source_sha(kind: str) -> str:
+def source_sha(kernel: str) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES[kind]:
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "attention_kl_divergence_skl_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def kernel_traffic(kind: str, workload: str):
-    """HBM bytes per launch from the committed PMC summary, only if it was
-    taken on the current kernel source; else None."""
+def kernel_traffic(kernel: str, phase: str, workload: str):
+    """HBM bytes per launch (FETCH + WRITE, calibrated) from the committed
+    counter summary, only if it was taken on the current kernel source.
+
+    Lines of the summary look like
+      traffic <workload> <phase> <kernel> <source_sha> <bytes_per_launch>
+    """
     try:
         with open(TRAFFIC_FILE) as fh:
-            data = json.load(fh)
-    except (OSError, ValueError):
+            lines = fh.read().splitlines()
+    except OSError:
         return None
-    ent = data.get(workload, {}).get(kind)
-    if not ent or ent.get("source_sha") != source_sha(kind):
-        return None
-    return ent.get("hbm_bytes_per_launch")
+    sha = source_sha(kernel)
+    for ln in lines:
+        f = ln.split()
+        if len(f) == 6 and f[0] == "traffic" and f[1:5] == [workload, phase, kernel, sha]:
+            return float(f[5])
+    return None
 
 
 def cpu_baseline(w, n_sub: int):
@@ -115,6 +122,18 @@ def copy_calibration(nbytes: int, reps: int) -> None:
     print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps}), flush=True)
 
 
+def kernel_flops(w, wk, phase: str, algo: str):
+    """Flops each main kernel of a phase must do (its own MFMA work)."""
+    P = wk.pairs
+    if phase == "fwd":
+        return {"fwd_kernel": wk.fwd_flops}
+    dg = w.d2 if phase == "student" else w.d1
+    if algo == "split":
+        per = 2 * P * (w.d1 + w.d2 + dg)  # both logits again + one gradient GEMM
+        return {"bwd_dk_kernel": per, "bwd_dq_kernel": per}
+    return {"bwd_fused_kernel": wk.student_flops if phase == "student" else wk.teacher_flops}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -123,6 +142,7 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--phases", default="fwd,student,teacher",
                     help="comma list of fwd, student, teacher (profiling aid; the default is the full step)")
+    ap.add_argument("--bwd-algo", default="split", choices=["split", "fused_atomic"])
     ap.add_argument("--cpu-sub", type=int, default=16384, help="side of the causal block the oracle times")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MiB",
@@ -155,6 +175,7 @@ def main(argv=None) -> int:
     for p in phases:
         if p not in ("fwd", "student", "teacher"):
             raise SystemExit(f"unknown phase {p}")
+    algo = args.bwd_algo
     log(f"workload {w.name}: generating inputs")
     t0 = time.perf_counter()
     t = synth.device_inputs(w, "cuda")
@@ -164,41 +185,47 @@ def main(argv=None) -> int:
     ebytes = 2 if w.dtype == "bf16" else 4
     wk = workmodel.work(w.B, w.H, w.NQ, w.NK, w.d1, w.d2, w.causal, ebytes)
 
-    # Workspaces are allocated once, outside the timed region.
-    ws_s = torch.empty(skl.skl_backward_workspace_size(q1, k1, q2, k2, False) // 4, dtype=torch.float32,
-                       device="cuda")
-    ws_t = torch.empty(skl.skl_backward_workspace_size(q1, k1, q2, k2, True) // 4, dtype=torch.float32,
-                       device="cuda")
+    # Workspaces (fused algorithm only) are allocated once, outside the timed region.
+    def ws_for(teacher):
+        n = skl.skl_backward_workspace_size(q1, k1, q2, k2, teacher, algo)
+        return torch.empty(n // 4, dtype=torch.float32, device="cuda") if n else None
 
-    ev = {p: [] for p in phases}        # main-kernel events
-    pev = {p: [] for p in phases}       # whole-call events
+    ws_s, ws_t = ws_for(False), ws_for(True)
+    kflops = {p: kernel_flops(w, wk, p, algo) for p in phases}
+    kev = {p: [] for p in phases}   # per call: events around its main kernels
+    pev = {p: [] for p in phases}   # per call: events around the whole call
+
+    def new_events(n):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for x in e:
+            x.record()  # torch creates the HIP event on first record; the library re-records
+        return e
 
     def step(record: bool):
         out = {}
         kl = l1 = l2 = None
         for p in ("fwd", "student", "teacher"):
-            need = p in phases or (p == "fwd" and phases != ["fwd"])
-            if not need:
+            if not (p in phases or (p == "fwd" and phases != ["fwd"])):
                 continue
-            if record and p in phases:
-                e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-                e[0].record()   # torch creates the HIP event on first record;
-                e[1].record()   # the library re-records both around its kernel
-                skl.skl_set_kernel_events(e[0], e[1])
-                e[2].record()
+            rec = record and p in phases
+            if rec:
+                ke = new_events(len(kflops[p]) + 1)
+                ce = new_events(2)
+                skl.skl_set_kernel_events(ke)
+                ce[0].record()
             if p == "fwd":
                 kl, l1, l2 = skl.skl_forward(q1, k1, q2, k2, w.scale1, w.scale2, w.causal)
             elif p == "student":
                 out["s"] = skl.skl_backward_student(q1, k1, q2, k2, l1, l2, g, w.scale1, w.scale2, w.causal,
-                                                    ws=ws_s)
+                                                    algo=algo, ws=ws_s)
             else:
                 out["t"] = skl.skl_backward_teacher(q1, k1, q2, k2, l1, l2, kl, g, w.scale1, w.scale2,
-                                                    w.causal, ws=ws_t)
-            if record and p in phases:
-                e[3].record()
-                skl.skl_set_kernel_events(None, None)
-                ev[p].append((e[0], e[1]))
-                pev[p].append((e[2], e[3]))
+                                                    w.causal, algo=algo, ws=ws_t)
+            if rec:
+                ce[1].record()
+                skl.skl_set_kernel_events([])
+                kev[p].append(ke)
+                pev[p].append(ce)
         return out
 
     # Extra HBM of one step: peak allocation beyond resident inputs and outputs.
@@ -210,7 +237,8 @@ def main(argv=None) -> int:
     peak = torch.cuda.max_memory_allocated() - base
     out_bytes = 3 * w.B * w.H * w.NQ * 4
     out_bytes += sum(x.numel() * x.element_size() for v in o.values() for x in v)
-    extra = peak - out_bytes + ws_s.numel() * 4 + ws_t.numel() * 4
+    held_ws = sum(x.numel() * 4 for x in (ws_s, ws_t) if x is not None)
+    extra = peak - out_bytes + held_ws
     del o
 
     for i in range(args.warmup):
@@ -225,20 +253,23 @@ def main(argv=None) -> int:
     elapsed = time.perf_counter() - t0
     log(f"{args.steps} timed steps in {elapsed:.3f} s")
 
-    ms = lambda pairs: float(np.mean([a.elapsed_time(b) for a, b in pairs]))  # noqa: E731
-    flops = {"fwd": wk.fwd_flops, "student": wk.student_flops, "teacher": wk.teacher_flops}
     peak_tf = workmodel.PEAK_BF16_DENSE_TFLOPS if w.dtype == "bf16" else workmodel.PEAK_FP32_MFMA_TFLOPS
-    kern = {}
+    alg = {"fwd": wk.fwd_flops, "student": wk.student_flops, "teacher": wk.teacher_flops}
+    report, kernels = {}, []
     for p in phases:
-        kms = ms(ev[p])
-        kern[p] = {"kernel_ms": kms, "call_ms": ms(pev[p]), "tflops": flops[p] / (kms * 1e-3) / 1e12}
-        kern[p]["pct_mfma_peak"] = 100.0 * kern[p]["tflops"] / peak_tf
-    step_flops = sum(flops[p] for p in phases)
+        call_ms = float(np.mean([a.elapsed_time(b) for a, b in pev[p]]))
+        ks = {}
+        for i, (name, fl) in enumerate(kflops[p].items()):
+            kms = float(np.mean([e[i].elapsed_time(e[i + 1]) for e in kev[p]]))
+            tf = fl / (kms * 1e-3) / 1e12
+            ks[name] = {"ms": kms, "tflops": tf, "pct_mfma_peak": 100.0 * tf / peak_tf}
+            kernels.append((kms, p, name, fl))
+        report[p] = {"call_ms": call_ms, "algorithmic_tflops": alg[p] / (call_ms * 1e-3) / 1e12,
+                     "kernels": ks}
+    step_flops = sum(alg[p] for p in phases)
     ms_step = elapsed / args.steps * 1e3
-    dom = max(phases, key=lambda p: kern[p]["kernel_ms"])
-    ach = kern[dom]["tflops"]
-    traffic = kernel_traffic(dom, w.name)
-    names = {"fwd": "fwd_kernel", "student": "bwd_kernel (student)", "teacher": "bwd_kernel (teacher)"}
+    kms, dom_phase, dom_name, dom_flops = max(kernels)
+    ach = dom_flops / (kms * 1e-3) / 1e12
     res = {
         "metric": METRIC,
         "value": step_flops / (ms_step * 1e-3) / 1e12,
@@ -253,19 +284,19 @@ def main(argv=None) -> int:
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N_Q": w.NQ, "N_K": w.NK, "d1": w.d1, "d2": w.d2,
-                   "causal": w.causal, "step": "+".join(phases)},
-        "phases": kern,
+                   "causal": w.causal, "step": "+".join(phases), "bwd_algo": algo},
+        "phases": report,
         "extra_hbm_bytes": int(extra),
         "materialised_bytes": int(wk.materialised_bytes),
         "roofline": {
-            "kernel": names[dom],
+            "kernel": f"{dom_name} ({dom_phase})",
             "bound": "mfma",
             "achieved": ach,
             "peak": peak_tf,
             "unit": "TFLOP/s",
             "frac": ach / peak_tf,
-            "traffic": traffic,
-            "algorithmic_flops_per_launch": flops[dom],
+            "traffic": kernel_traffic(dom_name, dom_phase, w.name),
+            "flops_per_launch": dom_flops,
         },
         "cpu_baseline": None,
     }

@@ -62,6 +62,18 @@ typedef enum skl_status {
 
 typedef enum skl_dtype { SKL_BF16 = 0, SKL_F32 = 1 } skl_dtype;
 
+/*
+ * Backward algorithms.
+ *  SKL_BWD_SPLIT (default): one kernel owns keys and writes dK, one owns
+ *    queries and writes dQ; both recompute the two logit tiles.  No
+ *    workspace, no atomics, bitwise deterministic.
+ *  SKL_BWD_FUSED_ATOMIC: one kernel visits each (query tile, key tile) pair
+ *    once, keeps dK on chip and adds dQ into an fp32 workspace with atomics
+ *    (article section "GPU kernel optimisations", fused backward); needs
+ *    skl_backward_workspace_size() bytes; dQ is not bitwise reproducible.
+ */
+typedef enum skl_bwd_algo { SKL_BWD_SPLIT = 0, SKL_BWD_FUSED_ATOMIC = 1 } skl_bwd_algo;
+
 /* Problem shape and input layout.  Strides are in elements. */
 typedef struct skl_shape {
   int64_t B, H, NQ, NK;
@@ -114,28 +126,28 @@ skl_status skl_reduce(const skl_shape* shape, int num_splits, const void* ws, si
                       float* kl, float* lse1, float* lse2, hipStream_t stream);
 
 /*
- * Size in bytes of the fp32 dQ accumulator a backward call needs:
- * 4 * B * H * N_Q * d, with d = d2 (teacher == 0) or d1 (teacher != 0).
+ * Workspace bytes a backward call with algorithm `algo` needs: 0 for
+ * SKL_BWD_SPLIT; for SKL_BWD_FUSED_ATOMIC the fp32 dQ accumulator,
+ * 4 * B * H * N_Q * d with d = d2 (teacher == 0) or d1 (teacher != 0).
  */
-size_t skl_backward_workspace_size(const skl_shape* shape, int teacher);
+size_t skl_backward_workspace_size(const skl_shape* shape, int teacher, int algo);
 
 /*
  * Backward, "optimise P2" (the student, P1 fixed): with g_i = dkl[b,h,i],
  *   dS2 = g_i * (P2 - P1),  dQ2 = scale2 * dS2 K2,  dK2 = scale2 * dS2^T Q2,
  * where P_k = exp(S_k - LSE_k) is rebuilt tile by tile from lse1 and lse2
  * as written by skl_forward (article section "Backward: recompute-based
- * tile-by-tile gradients").  One fused kernel visits each (query tile, key
- * tile) pair once; dK2 is accumulated on chip and dQ2 through fp32 atomics
- * in `ws` (article section "GPU kernel optimisations", fused backward).
+ * tile-by-tile gradients"), with the kernels of `algo` (skl_bwd_algo).
  * dq2 and dk2 have the element type of the inputs and the same strides as
- * q2 and k2 respectively.  ws: skl_backward_workspace_size(shape, 0) bytes,
- * 16-byte aligned; it is cleared by the call.
+ * q2 and k2 respectively.  ws: skl_backward_workspace_size(shape, 0, algo)
+ * bytes, 16-byte aligned (may be NULL when that is 0); the call clears it.
  */
 skl_status skl_backward_student(const skl_shape* shape,
                                 const void* q1, const void* k1, const void* q2, const void* k2,
                                 float scale1, float scale2, int causal,
                                 const float* lse1, const float* lse2, const float* dkl,
-                                void* dq2, void* dk2, void* ws, size_t ws_bytes, hipStream_t stream);
+                                void* dq2, void* dk2, int algo, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
 
 /*
  * Backward, "optimise P1" (the teacher, P2 fixed):
@@ -144,14 +156,15 @@ skl_status skl_backward_student(const skl_shape* shape,
  * The log-ratio is never formed from log P, so probabilities that underflow
  * give exact zeros instead of NaN (article section "Backward:
  * recompute-based tile-by-tile gradients").  kl is the forward's output.
- * dq1/dk1 have the strides of q1/k1.  ws: skl_backward_workspace_size(shape, 1).
+ * dq1/dk1 have the strides of q1/k1.  algo and ws as for the student, with
+ * skl_backward_workspace_size(shape, 1, algo).
  */
 skl_status skl_backward_teacher(const skl_shape* shape,
                                 const void* q1, const void* k1, const void* q2, const void* k2,
                                 float scale1, float scale2, int causal,
                                 const float* lse1, const float* lse2, const float* kl,
-                                const float* dkl, void* dq1, void* dk1, void* ws, size_t ws_bytes,
-                                hipStream_t stream);
+                                const float* dkl, void* dq1, void* dk1, int algo, void* ws,
+                                size_t ws_bytes, hipStream_t stream);
 
 /*
  * Split count that fills a GPU with `num_cus` compute units for this shape
@@ -161,13 +174,16 @@ int skl_recommended_splits(const skl_shape* shape, int causal, int num_cus);
 
 /*
  * Profiling aid.  After this call, every entry point called on this thread
- * records `start` on its stream immediately before enqueueing its main
- * kernel (the forward, split-K forward or fused backward kernel; not the
- * workspace clear, the reduce or the dQ convert) and `stop` right after it,
- * so hipEventElapsedTime(start, stop) is that kernel's duration.  Pass NULL
- * for both to switch it off.  The events stay owned by the caller.
+ * records events[0] on its stream right before enqueueing its first main
+ * kernel and events[k] right after its k-th main kernel (k < count), so
+ * hipEventElapsedTime(events[k-1], events[k]) is the k-th kernel's duration.
+ * Main kernels: the forward or split-K forward kernel (one); the split
+ * backward's dK kernel then dQ kernel (two); the fused backward kernel
+ * (one).  Workspace clears, the reduce and the dQ convert are not counted.
+ * count = 0 switches it off; at most 4 events.  The events stay owned by the
+ * caller.
  */
-skl_status skl_set_kernel_events(hipEvent_t start, hipEvent_t stop);
+skl_status skl_set_kernel_events(hipEvent_t* events, int count);
 
 /* Static description of a status code. */
 const char* skl_status_string(skl_status status);

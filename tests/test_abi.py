@@ -102,8 +102,9 @@ def test_empty_problems_enqueue_nothing(lib):
 def test_workspace_sizes(lib):
     s = _shape(B=2, H=3, NQ=100, NK=50, d1=128, d2=64)
     assert lib.skl_forward_splitk_workspace_size(ctypes.byref(s), 4) == 5 * 2 * 3 * 4 * 100 * 4
-    assert lib.skl_backward_workspace_size(ctypes.byref(s), 0) == 2 * 3 * 100 * 64 * 4
-    assert lib.skl_backward_workspace_size(ctypes.byref(s), 1) == 2 * 3 * 100 * 128 * 4
+    assert lib.skl_backward_workspace_size(ctypes.byref(s), 0, 1) == 2 * 3 * 100 * 64 * 4
+    assert lib.skl_backward_workspace_size(ctypes.byref(s), 1, 1) == 2 * 3 * 100 * 128 * 4
+    assert lib.skl_backward_workspace_size(ctypes.byref(s), 0, 0) == 0   # split: no workspace
     assert lib.skl_forward_splitk_workspace_size(ctypes.byref(s), 0) == 0
 
 
@@ -116,13 +117,24 @@ def test_split_and_backward_validation(lib):
     assert st == INVALID
     st = lib.skl_reduce(ctypes.byref(s), 2, A, need - 1, A, A, A, None)
     assert st == WS_SMALL
-    wsb = lib.skl_backward_workspace_size(ctypes.byref(s), 0)
-    st = lib.skl_backward_student(ctypes.byref(s), *P, 0.1, 0.1, 0, A, A, A, A, A, A, wsb - 16, None)
+    wsb = lib.skl_backward_workspace_size(ctypes.byref(s), 0, 1)
+    st = lib.skl_backward_student(ctypes.byref(s), *P, 0.1, 0.1, 0, A, A, A, A, A, 1, A, wsb - 16, None)
     assert st == WS_SMALL
-    st = lib.skl_backward_teacher(ctypes.byref(s), *P, 0.1, 0.1, 0, A, A, None, A, A, A, A, wsb, None)
+    st = lib.skl_backward_teacher(ctypes.byref(s), *P, 0.1, 0.1, 0, A, A, None, A, A, A, 0, None, 0, None)
     assert st == INVALID   # kl is required by the teacher setting
-    st = lib.skl_backward_student(ctypes.byref(s), *P, 0.1, 0.1, 0, A, A, A, A + 8, A, A, wsb, None)
+    st = lib.skl_backward_student(ctypes.byref(s), *P, 0.1, 0.1, 0, A, A, A, A + 8, A, 0, None, 0, None)
     assert st == UNSUPPORTED   # misaligned dq2
+    st = lib.skl_backward_student(ctypes.byref(s), *P, 0.1, 0.1, 0, A, A, A, A, A, 7, None, 0, None)
+    assert st == INVALID   # unknown algorithm
+    st = lib.skl_backward_student(ctypes.byref(s), *P, 0.1, 0.1, 0, A, A, A, A, A, 1, None, wsb, None)
+    assert st == INVALID   # the fused algorithm needs its workspace
+
+
+def test_kernel_event_hook_validation(lib):
+    arr = (ctypes.c_void_p * 5)()
+    assert lib.skl_set_kernel_events(arr, 5) == INVALID
+    assert lib.skl_set_kernel_events(None, 2) == INVALID
+    assert lib.skl_set_kernel_events(None, 0) == OK
 
 
 def test_status_strings_and_version(lib):

@@ -50,18 +50,19 @@ def test_forward_matches_oracle(gpu_lib, w):
     check_rows(w.name, w, got, oracle_forward(w, x))
 
 
+@pytest.mark.parametrize("algo", ["split", "fused_atomic"])
 @pytest.mark.parametrize("setting", ["student", "teacher"])
 @pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
-def test_backward_matches_oracle(gpu_lib, w, setting):
-    say(f"[backward {setting}] {w.name}")
+def test_backward_matches_oracle(gpu_lib, w, setting, algo):
+    say(f"[backward {setting} {algo}] {w.name}")
     x, t = to_device(w)
     _, (kl, l1, l2) = gpu_forward(gpu_lib, w, t)
     if setting == "student":
         dq, dk = gpu_lib.skl_backward_student(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, t["g"],
-                                              w.scale1, w.scale2, w.causal)
+                                              w.scale1, w.scale2, w.causal, algo=algo)
     else:
         dq, dk = gpu_lib.skl_backward_teacher(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, kl, t["g"],
-                                              w.scale1, w.scale2, w.causal)
+                                              w.scale1, w.scale2, w.causal, algo=algo)
     torch.cuda.synchronize()
     rq, rk = oracle_backward(w, x, setting)
     check_grad(f"{w.name} dQ ({setting})", w, grad_to_np(dq), rq)
@@ -166,22 +167,41 @@ def test_low_occupancy_split_shape(gpu_lib):
     check_rows(w.name, w, got, oracle_forward(w, x))
 
 
-def test_backward_run_to_run_variation(gpu_lib):
-    """Atomic dQ accumulation changes only the rounding order."""
+@pytest.mark.parametrize("algo", ["split", "fused_atomic"])
+def test_backward_run_to_run_variation(gpu_lib, algo):
+    """The split backward is bitwise deterministic; atomic dQ accumulation
+    changes only the rounding order."""
     w = W("rerun", 1, 2, 384, 384, 128, 128, "bf16", True)
-    say("[backward rerun]")
+    say(f"[backward rerun {algo}]")
     x, t = to_device(w)
     _, (kl, l1, l2) = gpu_forward(gpu_lib, w, t)
     outs = []
     for _ in range(3):
         dq, dk = gpu_lib.skl_backward_student(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, t["g"],
-                                              w.scale1, w.scale2, w.causal)
+                                              w.scale1, w.scale2, w.causal, algo=algo)
         outs.append((dq.float().clone(), dk.float().clone()))
     torch.cuda.synchronize()
     for dq, dk in outs[1:]:
         assert torch.equal(dk, outs[0][1]), "dK is accumulated on chip: bitwise reproducible"
+        if algo == "split":
+            assert torch.equal(dq, outs[0][0])
         rel = float((dq - outs[0][0]).norm() / outs[0][0].norm())
         assert rel <= 1e-2 * 1e-2
+
+
+def test_split_and_fused_backward_agree(gpu_lib):
+    w = W("agree", 2, 2, 300, 300, 128, 64, "bf16", True, synth.Recipe("iid", amp1=2.0))
+    say("[backward split vs fused]")
+    x, t = to_device(w)
+    _, (kl, l1, l2) = gpu_forward(gpu_lib, w, t)
+    a = gpu_lib.skl_backward_teacher(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, kl, t["g"], w.scale1,
+                                     w.scale2, True, algo="split")
+    b = gpu_lib.skl_backward_teacher(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, kl, t["g"], w.scale1,
+                                     w.scale2, True, algo="fused_atomic")
+    torch.cuda.synchronize()
+    for x_, y_ in zip(a, b):
+        rel = float((x_.float() - y_.float()).norm() / y_.float().norm())
+        assert rel <= 1e-2
 
 
 def test_errors_raise_before_launch(gpu_lib):
