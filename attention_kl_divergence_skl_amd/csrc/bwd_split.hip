@@ -29,29 +29,32 @@ namespace skl {
 
 namespace {
 
-constexpr int kPad = 32;  // LDS row pad (bytes): conflict-free 16-byte and transposing reads
-
-// dS of one accumulator element from the two logits (raw dot products).
+// dS of one accumulator element from the two logits (raw dot products) and
+// the row constants L_k = LSE_k log2 e and, for the student, ga = g; for the
+// teacher ga = g ln2 and gb = g KL, so that
+//   student: g (P2 - P1)                      = ga (2^u2 - 2^u1)
+//   teacher: g P1 (ln2 (u1 - u2) - KL)        = 2^u1 (ga (u1 - u2) - gb)
 template <bool TEACHER>
-__device__ __forceinline__ float dS_of(float s1, float s2, float c1, float c2, float L1, float L2, float g,
-                                       float kl) {
+__device__ __forceinline__ float dS_of(float s1, float s2, float c1, float c2, float L1, float L2, float ga,
+                                       float gb) {
   const float u1 = fmaf(s1, c1, -L1);
   const float u2 = fmaf(s2, c2, -L2);
-  if (TEACHER) return g * exp2_hw(u1) * fmaf(kLn2, u1 - u2, -kl);
-  return g * (exp2_hw(u2) - exp2_hw(u1));
+  if (TEACHER) return exp2_hw(u1) * fmaf(ga, u1 - u2, -gb);
+  return ga * (exp2_hw(u2) - exp2_hw(u1));
 }
 
 }  // namespace
 
 // ---------------------------------------------------------------------------
 // dK kernel: 4 waves own 128 keys (32 each) of one (b, h) and walk the query
-// tiles of 32 rows that see them.  Per step each wave forms S = Q Kᵀ (32
-// queries x its 32 keys; key = accumulator column, K in registers), dS in fp32,
-// and dK += dSᵀ Q_g with dSᵀ straight from the accumulator registers and Q_g
-// from the LDS query tile.  Query tiles are double-buffered in LDS.
+// tiles of 64 rows that see them, 32 rows at a time.  Per block each wave forms
+// S = Q Kᵀ (32 queries x its 32 keys; key = accumulator column, K in
+// registers), dS in fp32, and dK += dSᵀ Q_g with dSᵀ straight from the
+// accumulator registers and Q_g from the LDS query tile.  Query tiles are
+// loaded straight into a double-buffered, swizzled LDS ring.
 // ---------------------------------------------------------------------------
 template <typename T, int D1, int D2, bool CAUSAL, bool TEACHER>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dk_kernel(const BwdParams p) {
+__global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dk_kernel(const BwdParams p) {
   using M = Mfma<T>;
   using frag = typename M::frag;
   constexpr int KC = M::KC, EPL = M::EPL;
@@ -59,16 +62,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dk_kernel(const BwdParams p) 
   constexpr int DG = TEACHER ? D1 : D2;
   constexpr int NCB = DG / 32;
   constexpr int ESZ = sizeof(T);
-  constexpr int BQ = kBwdBQ;
-  constexpr int PQ1 = D1 * ESZ + kPad, PQ2 = D2 * ESZ + kPad;
-  constexpr int PQG = TEACHER ? PQ1 : PQ2;
-  constexpr int CPR1 = D1 * ESZ / 16, CPR2 = D2 * ESZ / 16;
-  constexpr int NL1 = (BQ * CPR1 + kThreads - 1) / kThreads;  // 16-byte loads per thread
-  constexpr int NL2 = (BQ * CPR2 + kThreads - 1) / kThreads;
+  constexpr int BQ = kDkBQ;
+  constexpr int RB1 = D1 * ESZ, RB2 = D2 * ESZ;  // bytes per query row
+  constexpr int RBG = TEACHER ? RB1 : RB2;
+  using T1 = SwzTile<RB1>;
+  using T2 = SwzTile<RB2>;
+  using TG = SwzTile<RBG>;
 
-  __shared__ __attribute__((aligned(16))) char sQ1[2][BQ * PQ1];
-  __shared__ __attribute__((aligned(16))) char sQ2[2][BQ * PQ2];
-  __shared__ __attribute__((aligned(16))) float sVec[2][4][BQ];  // L1, L2 (base 2), g, KL
+  __shared__ __attribute__((aligned(1024))) char sQ1[2][BQ * RB1];
+  __shared__ __attribute__((aligned(1024))) char sQ2[2][BQ * RB2];
+  __shared__ __attribute__((aligned(16))) float sVec[2][4][BQ];  // L1, L2 (base 2), ga, gb (see dS_of)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -105,23 +108,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dk_kernel(const BwdParams p) 
   if (CAUSAL) qbeg = max((int64_t)0, kt0 - off) / BQ * BQ;
   const int64_t nsteps = (p.NQ - qbeg + BQ - 1) / BQ;
 
-  uint4 pf1[NL1], pf2[NL2];
+  // Query tiles go straight into a double-buffered LDS ring (loads of step
+  // i+1 in flight during step i); the four per-row constants go through one
+  // register per thread.
   float pv = 0.f;
-  auto fetch = [&](int64_t q0) {
-#pragma unroll
-    for (int i = 0; i < NL1; ++i) {
-      const int idx = tid + i * kThreads;
-      const int row = idx / CPR1, ch = idx % CPR1;
-      pf1[i] = make_uint4(0u, 0u, 0u, 0u);
-      if (idx < BQ * CPR1 && q0 + row < p.NQ) pf1[i] = ld16(q1p + (q0 + row) * p.sq1.n * ESZ + ch * 16);
-    }
-#pragma unroll
-    for (int i = 0; i < NL2; ++i) {
-      const int idx = tid + i * kThreads;
-      const int row = idx / CPR2, ch = idx % CPR2;
-      pf2[i] = make_uint4(0u, 0u, 0u, 0u);
-      if (idx < BQ * CPR2 && q0 + row < p.NQ) pf2[i] = ld16(q2p + (q0 + row) * p.sq2.n * ESZ + ch * 16);
-    }
+  auto fetch = [&](int st, int64_t q0) {
+    tile_load_async<BQ, RB1>(sQ1[st], q1p, p.sq1.n * ESZ, q0, p.NQ, wave, lane);
+    tile_load_async<BQ, RB2>(sQ2[st], q2p, p.sq2.n * ESZ, q0, p.NQ, wave, lane);
     pv = 0.f;
     if (tid < 4 * BQ) {
       const int which = tid / BQ, row = tid % BQ;
@@ -130,29 +123,20 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dk_kernel(const BwdParams p) 
         const int64_t o = bh * p.NQ + q;
         if (which == 0) pv = p.lse1[o] * kLog2e;
         else if (which == 1) pv = p.lse2[o] * kLog2e;
-        else if (which == 2) pv = p.dkl[o];
-        else if (TEACHER) pv = p.kl[o];
+        else if (which == 2) pv = TEACHER ? p.dkl[o] * kLn2 : p.dkl[o];
+        else if (TEACHER) pv = p.dkl[o] * p.kl[o];
       }
     }
   };
   auto stash = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < NL1; ++i) {
-      const int idx = tid + i * kThreads;
-      if (idx < BQ * CPR1) st16(&sQ1[st][(idx / CPR1) * PQ1 + (idx % CPR1) * 16], pf1[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < NL2; ++i) {
-      const int idx = tid + i * kThreads;
-      if (idx < BQ * CPR2) st16(&sQ2[st][(idx / CPR2) * PQ2 + (idx % CPR2) * 16], pf2[i]);
-    }
     if (tid < 4 * BQ) sVec[st][tid / BQ][tid % BQ] = pv;
   };
 
   if (nsteps > 0) {
-    fetch(qbeg);
+    fetch(0, qbeg);
     stash(0);
   }
+  wait_vm();
   __syncthreads();
   const float c1 = p.c1, c2 = p.c2;
   const int prow = rperm(col);
@@ -160,63 +144,71 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dk_kernel(const BwdParams p) 
   for (int64_t it = 0; it < nsteps; ++it) {
     const int st = (int)(it & 1);
     const int64_t q0 = qbeg + it * BQ;
-    if (it + 1 < nsteps) fetch(q0 + BQ);  // next tile in flight during this step
+    if (it + 1 < nsteps) fetch(st ^ 1, q0 + BQ);  // next tile in flight during this step
 
-    const bool live = kw0 < p.NK && (!CAUSAL || kw0 <= q0 + BQ - 1 + off);
-    if (live) {
+    const char* qg = TEACHER ? &sQ1[st][0] : &sQ2[st][0];
+#pragma unroll
+    for (int qb = 0; qb < BQ / 32; ++qb) {
+      const int64_t qb0 = q0 + 32 * qb;
+      if (kw0 >= p.NK || qb0 >= p.NQ || (CAUSAL && kw0 > qb0 + 31 + off)) continue;  // block fully masked
       f32x16 s1 = f32x16{}, s2 = f32x16{};
-      const char* a1 = &sQ1[st][prow * PQ1 + half * EPL * ESZ];
-      const char* a2 = &sQ2[st][prow * PQ2 + half * EPL * ESZ];
+      const int qrow = 32 * qb + prow;
 #pragma unroll
-      for (int c = 0; c < NC1; ++c) s1 = M::run(M::load(a1 + c * KC * ESZ), kf1[c], s1);
+      for (int c = 0; c < NC1; ++c)
+        s1 = M::run(M::load(&sQ1[st][T1::off(qrow, (c * KC + half * EPL) * ESZ)]), kf1[c], s1);
 #pragma unroll
-      for (int c = 0; c < NC2; ++c) s2 = M::run(M::load(a2 + c * KC * ESZ), kf2[c], s2);
+      for (int c = 0; c < NC2; ++c)
+        s2 = M::run(M::load(&sQ2[st][T2::off(qrow, (c * KC + half * EPL) * ESZ)]), kf2[c], s2);
 
-      // Per-row values for the 16 rows this lane holds (two runs of 8).
-      float vL1[16], vL2[16], vg[16], vkl[16];
+      // Registers 8 run .. 8 run + 7 hold rows 32 qb + 16 run + 8 half + 0..7:
+      // their row constants are two float4 reads, and they form K chunk
+      // `run` (bf16) or chunks 8 run .. 8 run + 7 (fp32) of dK += dSᵀ Q_g, so
+      // each run is converted and consumed right away.
+      const bool need_mask = (qb0 + 32 > p.NQ) || (kw0 + 32 > p.NK) || (CAUSAL && kw0 + 31 > qb0 + off);
+      // Row qb0 + ro sees this lane's key iff ro < NQ - qb0 and (causal) ro >= key - qb0 - off.
+      const int qlim = clamp_i32(p.NQ - qb0), cmin = clamp_i32(key - qb0 - off);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ql = rloc(r, half);
-        vL1[r] = sVec[st][0][ql];
-        vL2[r] = sVec[st][1][ql];
-        vg[r] = sVec[st][2][ql];
-        vkl[r] = TEACHER ? sVec[st][3][ql] : 0.f;
-      }
-      const bool need_mask = (q0 + BQ > p.NQ) || (kw0 + 32 > p.NK) || (CAUSAL && kw0 + 31 > q0 + off);
-      f32x16 ds;
+      for (int run = 0; run < 2; ++run) {
+        float cst[4][8];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = dS_of<TEACHER>(s1[r], s2[r], c1, c2, vL1[r], vL2[r], vg[r], vkl[r]);
-        if (need_mask) {
-          const int64_t q = q0 + rloc(r, half);
-          v = (q < p.NQ && kvalid && (!CAUSAL || key <= q + off)) ? v : 0.f;
+        for (int which = 0; which < (TEACHER ? 4 : 3); ++which) {
+          const float4* v = reinterpret_cast<const float4*>(&sVec[st][which][32 * qb + 16 * run + 8 * half]);
+          const float4 x0 = v[0], x1 = v[1];
+          cst[which][0] = x0.x; cst[which][1] = x0.y; cst[which][2] = x0.z; cst[which][3] = x0.w;
+          cst[which][4] = x1.x; cst[which][5] = x1.y; cst[which][6] = x1.z; cst[which][7] = x1.w;
         }
-        ds[r] = v;
-      }
-
-      const char* qg = TEACHER ? &sQ1[st][0] : &sQ2[st][0];
+        float ds[8];
 #pragma unroll
-      for (int c = 0; c < BQ / KC; ++c) {
-        frag a;
-        if constexpr (EPL == 1) {
-          a = ds[c];
-        } else {
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) a[e] = from_f32<T>(ds[c * EPL + e]);
-        }
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          frag bq;
-          if constexpr (EPL == 1) {
-            bq = *reinterpret_cast<const float*>(qg + rloc(c, half) * PQG + (32 * cb + col) * ESZ);
-          } else {
-            bq = lds_tr_frag(qg, PQG, c * KC, 32 * cb, lane);
+        for (int i = 0; i < 8; ++i) {
+          const int r = 8 * run + i;
+          float v = dS_of<TEACHER>(s1[r], s2[r], c1, c2, cst[0][i], cst[1][i], cst[2][i], TEACHER ? cst[3][i] : 0.f);
+          if (need_mask) {
+            const int ro = rloc(r, half);
+            v = (kvalid && ro < qlim && (!CAUSAL || ro >= cmin)) ? v : 0.f;
           }
-          dk[cb] = M::run(a, bq, dk[cb]);
+          ds[i] = v;
+        }
+        if constexpr (EPL == 1) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int c = 8 * run + i;
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+              const float bq = *reinterpret_cast<const float*>(qg + TG::off(32 * qb + rloc(c, half), (32 * cb + col) * ESZ));
+              dk[cb] = M::run(ds[i], bq, dk[cb]);
+            }
+          }
+        } else {
+          frag a;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) a[e] = from_f32<T>(ds[e]);
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) dk[cb] = M::run(a, lds_tr_frag_swz<RBG>(qg, 32 * qb + run * KC, 32 * cb, lane), dk[cb]);
         }
       }
     }
     if (it + 1 < nsteps) stash(st ^ 1);
+    wait_vm();
     __syncthreads();
   }
 
@@ -240,7 +232,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dk_kernel(const BwdParams p) 
 // the LDS key tile.  Key tiles are double-buffered in LDS.
 // ---------------------------------------------------------------------------
 template <typename T, int D1, int D2, bool CAUSAL, bool TEACHER>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(const BwdParams p) {
+__global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kernel(const BwdParams p) {
   using M = Mfma<T>;
   using frag = typename M::frag;
   constexpr int KC = M::KC, EPL = M::EPL;
@@ -249,14 +241,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(const BwdParams p) 
   constexpr int NCB = DG / 32;
   constexpr int ESZ = sizeof(T);
   constexpr int BQ = 128, BK = kDqBK;
-  constexpr int PK1 = D1 * ESZ + kPad, PK2 = D2 * ESZ + kPad;
-  constexpr int PKG = TEACHER ? PK1 : PK2;
-  constexpr int CPR1 = D1 * ESZ / 16, CPR2 = D2 * ESZ / 16;
-  constexpr int NL1 = (BK * CPR1 + kThreads - 1) / kThreads;
-  constexpr int NL2 = (BK * CPR2 + kThreads - 1) / kThreads;
+  constexpr int RB1 = D1 * ESZ, RB2 = D2 * ESZ;  // bytes per key row
+  constexpr int RBG = TEACHER ? RB1 : RB2;
+  using T1 = SwzTile<RB1>;
+  using T2 = SwzTile<RB2>;
+  using TG = SwzTile<RBG>;
 
-  __shared__ __attribute__((aligned(16))) char sK1[2][BK * PK1];
-  __shared__ __attribute__((aligned(16))) char sK2[2][BK * PK2];
+  __shared__ __attribute__((aligned(1024))) char sK1[2][BK * RB1];
+  __shared__ __attribute__((aligned(1024))) char sK2[2][BK * RB2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -287,13 +279,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(const BwdParams p) 
     qf2[c] = qvalid ? M::load(q2p + (qi * p.sq2.n + c * KC + half * EPL) * ESZ) : M::zero();
 
   // Per-row constants: this lane's query row.
-  float L1 = 0.f, L2 = 0.f, g = 0.f, klv = 0.f;
+  float L1 = 0.f, L2 = 0.f, ga = 0.f, gb = 0.f;
   if (qvalid) {
     const int64_t o = bh * p.NQ + qi;
     L1 = p.lse1[o] * kLog2e;
     L2 = p.lse2[o] * kLog2e;
-    g = p.dkl[o];
-    if (TEACHER) klv = p.kl[o];
+    ga = TEACHER ? p.dkl[o] * kLn2 : p.dkl[o];
+    if (TEACHER) gb = p.dkl[o] * p.kl[o];
   }
 
   f32x16 dq[NCB];
@@ -305,40 +297,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(const BwdParams p) 
   const int64_t nsteps = (kend + BK - 1) / BK;
   const int64_t wave_kmax = CAUSAL ? qw0 + 31 + off : p.NK - 1;
 
-  uint4 pf1[NL1], pf2[NL2];
-  auto fetch = [&](int64_t j0) {
-#pragma unroll
-    for (int i = 0; i < NL1; ++i) {
-      const int idx = tid + i * kThreads;
-      const int row = idx / CPR1, ch = idx % CPR1;
-      pf1[i] = make_uint4(0u, 0u, 0u, 0u);
-      if (idx < BK * CPR1 && j0 + row < p.NK) pf1[i] = ld16(k1p + (j0 + row) * p.sk1.n * ESZ + ch * 16);
-    }
-#pragma unroll
-    for (int i = 0; i < NL2; ++i) {
-      const int idx = tid + i * kThreads;
-      const int row = idx / CPR2, ch = idx % CPR2;
-      pf2[i] = make_uint4(0u, 0u, 0u, 0u);
-      if (idx < BK * CPR2 && j0 + row < p.NK) pf2[i] = ld16(k2p + (j0 + row) * p.sk2.n * ESZ + ch * 16);
-    }
-  };
-  auto stash = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < NL1; ++i) {
-      const int idx = tid + i * kThreads;
-      if (idx < BK * CPR1) st16(&sK1[st][(idx / CPR1) * PK1 + (idx % CPR1) * 16], pf1[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < NL2; ++i) {
-      const int idx = tid + i * kThreads;
-      if (idx < BK * CPR2) st16(&sK2[st][(idx / CPR2) * PK2 + (idx % CPR2) * 16], pf2[i]);
-    }
+  auto fetch = [&](int st, int64_t j0) {
+    tile_load_async<BK, RB1>(sK1[st], k1p, p.sk1.n * ESZ, j0, p.NK, wave, lane);
+    tile_load_async<BK, RB2>(sK2[st], k2p, p.sk2.n * ESZ, j0, p.NK, wave, lane);
   };
 
-  if (nsteps > 0) {
-    fetch(0);
-    stash(0);
-  }
+  if (nsteps > 0) fetch(0, 0);
+  wait_vm();
   __syncthreads();
   const float c1 = p.c1, c2 = p.c2;
   const int prow = rperm(col);
@@ -346,7 +311,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(const BwdParams p) 
   for (int64_t it = 0; it < nsteps; ++it) {
     const int st = (int)(it & 1);
     const int64_t j0 = it * BK;
-    if (it + 1 < nsteps) fetch(j0 + BK);
+    if (it + 1 < nsteps) fetch(st ^ 1, j0 + BK);
 
     if (j0 <= wave_kmax) {
       const bool need_mask = (j0 + BK > p.NK) || (CAUSAL && j0 + BK - 1 > qw0 + off) || (qw0 + 32 > p.NQ);
@@ -354,45 +319,53 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(const BwdParams p) 
 #pragma unroll
       for (int kb = 0; kb < BK / 32; ++kb) {
         f32x16 s1 = f32x16{}, s2 = f32x16{};
-        const char* a1 = &sK1[st][(kb * 32 + prow) * PK1 + half * EPL * ESZ];
-        const char* a2 = &sK2[st][(kb * 32 + prow) * PK2 + half * EPL * ESZ];
+        const int krow = kb * 32 + prow;
+        // Key j0 + 32 kb + ro is visible iff ro < NK - jb and (causal) ro <= qi + off - jb.
+        const int klim = clamp_i32(p.NK - (j0 + kb * 32)), cmax = clamp_i32(qi + off - (j0 + kb * 32));
 #pragma unroll
-        for (int c = 0; c < NC1; ++c) s1 = M::run(M::load(a1 + c * KC * ESZ), qf1[c], s1);
+        for (int c = 0; c < NC1; ++c)
+          s1 = M::run(M::load(&sK1[st][T1::off(krow, (c * KC + half * EPL) * ESZ)]), qf1[c], s1);
 #pragma unroll
-        for (int c = 0; c < NC2; ++c) s2 = M::run(M::load(a2 + c * KC * ESZ), qf2[c], s2);
-        f32x16 ds;
+        for (int c = 0; c < NC2; ++c)
+          s2 = M::run(M::load(&sK2[st][T2::off(krow, (c * KC + half * EPL) * ESZ)]), qf2[c], s2);
+        // Registers 8 run .. 8 run + 7 hold keys kb 32 + 16 run + 8 half + 0..7:
+        // K chunk `run` (bf16) or chunks 8 run .. 8 run + 7 (fp32) of
+        // dQ += dS K_g, consumed as soon as they are formed.
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = dS_of<TEACHER>(s1[r], s2[r], c1, c2, L1, L2, g, klv);
-          if (need_mask) {
-            const int64_t kk = j0 + kb * 32 + rloc(r, half);
-            v = (qvalid && kk < p.NK && (!CAUSAL || kk <= qi + off)) ? v : 0.f;
-          }
-          ds[r] = v;
-        }
+        for (int run = 0; run < 2; ++run) {
+          float ds[8];
 #pragma unroll
-        for (int c = 0; c < 32 / KC; ++c) {
-          frag a;
-          if constexpr (EPL == 1) {
-            a = ds[c];
-          } else {
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) a[e] = from_f32<T>(ds[c * EPL + e]);
-          }
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) {
-            frag bk;
-            if constexpr (EPL == 1) {
-              bk = *reinterpret_cast<const float*>(kg + (kb * 32 + rloc(c, half)) * PKG + (32 * cb + col) * ESZ);
-            } else {
-              bk = lds_tr_frag(kg, PKG, kb * 32 + c * KC, 32 * cb, lane);
+          for (int i = 0; i < 8; ++i) {
+            const int r = 8 * run + i;
+            float v = dS_of<TEACHER>(s1[r], s2[r], c1, c2, L1, L2, ga, gb);
+            if (need_mask) {
+              const int ro = rloc(r, half);
+              v = (qvalid && ro < klim && (!CAUSAL || ro <= cmax)) ? v : 0.f;
             }
-            dq[cb] = M::run(a, bk, dq[cb]);
+            ds[i] = v;
+          }
+          if constexpr (EPL == 1) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const int c = 8 * run + i;
+#pragma unroll
+              for (int cb = 0; cb < NCB; ++cb) {
+                const float bk = *reinterpret_cast<const float*>(kg + TG::off(kb * 32 + rloc(c, half), (32 * cb + col) * ESZ));
+                dq[cb] = M::run(ds[i], bk, dq[cb]);
+              }
+            }
+          } else {
+            frag a;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) a[e] = from_f32<T>(ds[e]);
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+              dq[cb] = M::run(a, lds_tr_frag_swz<RBG>(kg, kb * 32 + run * KC, 32 * cb, lane), dq[cb]);
           }
         }
       }
     }
-    if (it + 1 < nsteps) stash(st ^ 1);
+    wait_vm();
     __syncthreads();
   }
 

@@ -18,8 +18,11 @@
 // keys of every 32-key block.  Row reductions are then in-lane; the two lane
 // halves hold disjoint key subsets of the same row and run their own online
 // statistics, merged once at the end.  Q fragments stay in registers for the
-// whole key loop; K tiles are staged in LDS (padded rows, conflict-free 16-byte
-// reads) and shared by the 4 waves.
+// whole key loop; K tiles are loaded straight into LDS (direct-to-LDS loads,
+// XOR-swizzled rows for conflict-free 16-byte reads), shared by the 4 waves and
+// double-buffered: the loads of the next tile are issued before the current
+// one is computed.  The online update
+// runs per 32-key block (one max, two correction factors per block and row).
 //
 // Split-K (article section "GPU kernel optimisations"): the same kernel over a
 // contiguous key range writes the five per-row partials (m1, l1, m2, l2, acc)
@@ -37,13 +40,12 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(c
   constexpr int KC = M::KC, EPL = M::EPL;
   constexpr int NC1 = D1 / KC, NC2 = D2 / KC;
   constexpr int ESZ = sizeof(T);
-  constexpr int PITCH1 = D1 * ESZ + 16;  // LDS row pitch in bytes (16-byte pad)
-  constexpr int PITCH2 = D2 * ESZ + 16;
-  constexpr int CPR1 = D1 * ESZ / 16;    // 16-byte chunks per key row
-  constexpr int CPR2 = D2 * ESZ / 16;
-  __shared__ __attribute__((aligned(16))) char smem[kFwdBK * (PITCH1 + PITCH2)];
-  char* const sk1 = smem;
-  char* const sk2 = smem + kFwdBK * PITCH1;
+  constexpr int BK = kFwdBK;
+  constexpr int RB1 = D1 * ESZ, RB2 = D2 * ESZ;  // bytes per key row
+  using T1 = SwzTile<RB1>;
+  using T2 = SwzTile<RB2>;
+  __shared__ __attribute__((aligned(1024))) char sK1[2][BK * RB1];
+  __shared__ __attribute__((aligned(1024))) char sK2[2][BK * RB2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -87,102 +89,98 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(c
     kbeg = (int64_t)split * p.split_len;
     kend = min(kend, kbeg + (int64_t)p.split_len);
   }
+  const int64_t nsteps = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
   const int64_t wave_kmax = CAUSAL ? qw0 + 31 + off : p.NK - 1;  // last key any row of the wave sees
+
+  // Key tiles are loaded straight into a double-buffered LDS ring: the loads
+  // of tile i+1 are in flight while tile i is computed; one barrier per tile.
+  auto fetch = [&](int st, int64_t j0) {
+    tile_load_async<BK, RB1>(sK1[st], k1p, p.sk1.n * ESZ, j0, p.NK, wave, lane);
+    tile_load_async<BK, RB2>(sK2[st], k2p, p.sk2.n * ESZ, j0, p.NK, wave, lane);
+  };
 
   const float c1 = p.c1, c2 = p.c2;
   float m1 = neg_inf(), m2 = neg_inf(), l1 = 0.f, l2 = 0.f, acc = 0.f;
 
-  for (int64_t j0 = kbeg; j0 < kend; j0 += kFwdBK) {
-    __syncthreads();  // previous tile fully consumed
-    for (int idx = tid; idx < kFwdBK * CPR1; idx += kThreads) {
-      const int row = idx / CPR1, ch = idx % CPR1;
-      const int64_t key = j0 + row;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (key < p.NK) v = ld16(k1p + key * p.sk1.n * ESZ + ch * 16);
-      st16(sk1 + row * PITCH1 + ch * 16, v);
-    }
-    for (int idx = tid; idx < kFwdBK * CPR2; idx += kThreads) {
-      const int row = idx / CPR2, ch = idx % CPR2;
-      const int64_t key = j0 + row;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (key < p.NK) v = ld16(k2p + key * p.sk2.n * ESZ + ch * 16);
-      st16(sk2 + row * PITCH2 + ch * 16, v);
-    }
-    __syncthreads();
-    if (j0 > wave_kmax) continue;  // the whole tile is masked for this wave
+  if (nsteps > 0) fetch(0, kbeg);
+  wait_vm();
+  __syncthreads();
 
-    f32x16 s1[2], s2[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s1[kb] = f32x16{};
-      s2[kb] = f32x16{};
-      const char* a1 = sk1 + (kb * 32 + col) * PITCH1 + half * EPL * ESZ;
-      const char* a2 = sk2 + (kb * 32 + col) * PITCH2 + half * EPL * ESZ;
-#pragma unroll
-      for (int c = 0; c < NC1; ++c) s1[kb] = M::run(M::load(a1 + c * KC * ESZ), qf1[c], s1[kb]);
-#pragma unroll
-      for (int c = 0; c < NC2; ++c) s2[kb] = M::run(M::load(a2 + c * KC * ESZ), qf2[c], s2[kb]);
-    }
+  for (int64_t it = 0; it < nsteps; ++it) {
+    const int st = (int)(it & 1);
+    const int64_t j0 = kbeg + it * BK;
+    if (it + 1 < nsteps) fetch(st ^ 1, j0 + BK);
 
-    const bool need_mask = (j0 + kFwdBK > p.NK) || (CAUSAL && j0 + kFwdBK - 1 > qw0 + off);
-    if (need_mask) {
+    if (j0 <= wave_kmax) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < BK / 32; ++kb) {
+        const int64_t jb = j0 + kb * 32;
+        if (jb > wave_kmax) break;  // the rest of the tile is masked for this wave
+        f32x16 s1 = f32x16{}, s2 = f32x16{};
+        const int krow = kb * 32 + col;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t key = j0 + kb * 32 + acc_row(r, half);
-          const bool ok = key < p.NK && (!CAUSAL || key <= qi + off);
-          if (!ok) {
-            s1[kb][r] = neg_inf();
-            s2[kb][r] = neg_inf();
+        for (int c = 0; c < NC1; ++c)
+          s1 = M::run(M::load(&sK1[st][T1::off(krow, (c * KC + half * EPL) * ESZ)]), qf1[c], s1);
+#pragma unroll
+        for (int c = 0; c < NC2; ++c)
+          s2 = M::run(M::load(&sK2[st][T2::off(krow, (c * KC + half * EPL) * ESZ)]), qf2[c], s2);
+
+        const bool need_mask = (jb + 32 > p.NK) || (CAUSAL && jb + 31 > qw0 + off);
+        if (need_mask) {
+          // Key jb + ro is visible iff ro < NK - jb and (causal) ro <= qi + off - jb.
+          const int klim = clamp_i32(p.NK - jb), cmax = clamp_i32(qi + off - jb);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int ro = acc_row(r, half);
+            if (!(ro < klim && (!CAUSAL || ro <= cmax))) {
+              s1[r] = neg_inf();
+              s2[r] = neg_inf();
+            }
           }
         }
-    }
 
-    float mx1 = neg_inf(), mx2 = neg_inf();
+        float mx1 = neg_inf(), mx2 = neg_inf();
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+        for (int r = 0; r < 16; ++r) {
+          mx1 = fmaxf(mx1, s1[r]);
+          mx2 = fmaxf(mx2, s2[r]);
+        }
+        const float m1n = fmaxf(m1, mx1 * c1), m2n = fmaxf(m2, mx2 * c2);
+        const float m1u = (m1n == neg_inf()) ? 0.f : m1n;  // no key seen yet: keep sums at 0
+        const float m2u = (m2n == neg_inf()) ? 0.f : m2n;
+        const float a1f = exp2_hw(m1 - m1u), a2f = exp2_hw(m2 - m2u);
+
+        float sum1 = 0.f, sum2 = 0.f, accd = 0.f;
+        if (need_mask) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        mx1 = fmaxf(mx1, s1[kb][r]);
-        mx2 = fmaxf(mx2, s2[kb][r]);
+          for (int r = 0; r < 16; ++r) {
+            const float u1 = fmaf(s1[r], c1, -m1u), u2 = fmaf(s2[r], c2, -m2u);
+            const float e1 = exp2_hw(u1), e2 = exp2_hw(u2);
+            sum1 += e1;
+            sum2 += e2;
+            const float d = (s1[r] == neg_inf()) ? 0.f : (u1 - u2);
+            accd = fmaf(e1, d, accd);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float u1 = fmaf(s1[r], c1, -m1u), u2 = fmaf(s2[r], c2, -m2u);
+            const float e1 = exp2_hw(u1), e2 = exp2_hw(u2);
+            sum1 += e1;
+            sum2 += e2;
+            accd = fmaf(e1, u1 - u2, accd);
+          }
+        }
+        // t1 - t2 = (u1 - u2) + (m1u - m2u): the per-row part is added once per block.
+        l1 = fmaf(l1, a1f, sum1);
+        l2 = fmaf(l2, a2f, sum2);
+        acc = fmaf(acc, a1f, fmaf(m1u - m2u, sum1, accd));
+        m1 = m1n;
+        m2 = m2n;
       }
-    const float m1n = fmaxf(m1, mx1 * c1), m2n = fmaxf(m2, mx2 * c2);
-    const float m1u = (m1n == neg_inf()) ? 0.f : m1n;  // no key seen yet: keep sums at 0
-    const float m2u = (m2n == neg_inf()) ? 0.f : m2n;
-    const float a1 = exp2_hw(m1 - m1u), a2 = exp2_hw(m2 - m2u);
-
-    float sum1 = 0.f, sum2 = 0.f, accd = 0.f;
-    if (need_mask) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float u1 = fmaf(s1[kb][r], c1, -m1u), u2 = fmaf(s2[kb][r], c2, -m2u);
-          const float e1 = exp2_hw(u1), e2 = exp2_hw(u2);
-          sum1 += e1;
-          sum2 += e2;
-          const float d = (s1[kb][r] == neg_inf()) ? 0.f : (u1 - u2);
-          accd = fmaf(e1, d, accd);
-        }
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float u1 = fmaf(s1[kb][r], c1, -m1u), u2 = fmaf(s2[kb][r], c2, -m2u);
-          const float e1 = exp2_hw(u1), e2 = exp2_hw(u2);
-          sum1 += e1;
-          sum2 += e2;
-          accd = fmaf(e1, u1 - u2, accd);
-        }
     }
-    // t1 - t2 = (u1 - u2) + (m1u - m2u): the per-row part is added once per tile.
-    l1 = fmaf(l1, a1, sum1);
-    l2 = fmaf(l2, a2, sum2);
-    acc = fmaf(acc, a1, fmaf(m1u - m2u, sum1, accd));
-    m1 = m1n;
-    m2 = m2n;
+    wait_vm();
+    __syncthreads();
   }
 
   // Merge the two lane halves (disjoint key subsets of the same row).

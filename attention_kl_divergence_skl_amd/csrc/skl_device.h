@@ -88,6 +88,73 @@ __device__ __forceinline__ bf16x8 lds_tr_frag(const char* tile, int pitch, int k
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// A tile of row-major rows held in LDS with no padding: row r occupies
+// [r * ROWB, (r + 1) * ROWB) and its 16-byte chunks are permuted by
+// chunk' = chunk ^ swz(r).  The permutation makes the two read patterns of the
+// kernels bank-conflict free on the 64 x 4-byte LDS banks: 16 lanes reading
+// the same logical chunk of 16 different rows, and a transposing read (4
+// consecutive rows x 2 adjacent chunks per 16-lane group).  fp32 tiles (512-byte
+// rows, only read one float per lane) stay unpermuted.
+template <int ROWB>
+struct SwzTile {
+  static constexpr int CPR = ROWB / 16;  // 16-byte chunks per row
+  __device__ __forceinline__ static int swz(int r) {
+    if constexpr (CPR == 16) return ((r & 7) << 1) | ((r >> 3) & 1);
+    else if constexpr (CPR == 8) return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
+    else return 0;
+  }
+  // Byte offset of logical byte `colb` of row r.
+  __device__ __forceinline__ static int off(int r, int colb) {
+    return r * ROWB + ((((colb >> 4) ^ swz(r)) << 4) | (colb & 15));
+  }
+};
+
+// Direct global -> LDS loads (gfx950 global_load_lds_dwordx4: lane i of a wave
+// writes its 16 bytes at the instruction's LDS base + 16 i, no registers) of
+// rows [j0, j0 + ROWS) of a row-major global tensor with row stride `rs`
+// bytes into a SwzTile<ROWB>.  Rows at or past `nrows` re-read the last row
+// (callers mask them out).  The 4 waves of the workgroup split the work; the
+// data is in LDS once each wave has waited for its loads (vmcnt 0) and the
+// workgroup has passed a barrier.
+template <int ROWS, int ROWB>
+__device__ __forceinline__ void tile_load_async(char* tile, const char* g, int64_t rs, int64_t j0, int64_t nrows,
+                                                int wave, int lane) {
+  using TL = SwzTile<ROWB>;
+  constexpr int RPI = 1024 / ROWB;      // rows per wave instruction
+  constexpr int NI = ROWS / RPI;        // instructions per tile
+  static_assert(NI % 4 == 0, "tile must split evenly over 4 waves");
+  const int pc = lane % TL::CPR;
+#pragma unroll
+  for (int k = 0; k < NI / 4; ++k) {
+    const int m = wave + 4 * k;
+    const int r = m * RPI + lane / TL::CPR;
+    const int lc = pc ^ TL::swz(r);
+    int64_t gr = j0 + r;
+    gr = gr < nrows ? gr : nrows - 1;
+    const char* src = g + gr * rs + lc * 16;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)(tile + m * 1024), 16, 0, 0);
+  }
+}
+
+// Wait until this wave's outstanding global loads (including direct-to-LDS
+// ones) have landed: s_waitcnt vmcnt(0).
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Transposing-read operand (see lds_tr_frag) from a SwzTile of bf16 rows.
+template <int ROWB>
+__device__ __forceinline__ bf16x8 lds_tr_frag_swz(const char* tile, int k0, int n0, int lane) {
+  using TL = SwzTile<ROWB>;
+  const int g = lane >> 4, L = lane & 15;
+  const int row = k0 + 8 * (g >> 1) + (L >> 2);
+  const int colb = 2 * (n0 + 16 * (g & 1) + 4 * (L & 3));
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + TL::off(row, colb)));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + TL::off(row + 4, colb)));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // 16-byte copy global -> LDS through registers.
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
@@ -98,6 +165,11 @@ template <>
 __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // RNE (v_cvt_pk_bf16_f32)
 template <>
 __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+
+// Clamp a 64-bit index difference into int range for 32-bit mask compares.
+__device__ __forceinline__ int clamp_i32(int64_t x) {
+  return (int)(x < -(int64_t(1) << 30) ? -(int64_t(1) << 30) : (x > (int64_t(1) << 30) ? (int64_t(1) << 30) : x));
+}
 
 // Map a linear workgroup id so that consecutive logical tiles land on the same
 // XCD: the hardware hands workgroup i to XCD i % 8, so logical tile

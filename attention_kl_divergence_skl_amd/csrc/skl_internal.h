@@ -13,6 +13,7 @@ constexpr int kFwdBK = 64;   // keys per forward pipeline step
 constexpr int kBwdBK = 128;  // keys per backward workgroup (4 waves x 32)
 constexpr int kBwdBQ = 32;   // queries per backward step (fused and dK kernels)
 constexpr int kDqBK = 64;    // keys per step of the dQ kernel
+constexpr int kDkBQ = 64;    // queries per step of the dK kernel
 constexpr int kThreads = 256;
 
 struct Strides {
