@@ -60,7 +60,8 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_fused_ke
   __shared__ __attribute__((aligned(16))) float sRed[KSPLIT > 1 ? NCB * 16 * 64 : 1];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
 
   const int64_t t = xcd_remap(blockIdx.x, gridDim.x);

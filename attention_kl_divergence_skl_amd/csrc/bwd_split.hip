@@ -74,7 +74,8 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dk_kerne
   __shared__ __attribute__((aligned(16))) float sVec[2][4][BQ];  // L1, L2 (base 2), ga, gb (see dS_of)
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
 
   const int64_t t = xcd_remap(blockIdx.x, gridDim.x);
@@ -251,7 +252,8 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kerne
   __shared__ __attribute__((aligned(1024))) char sK2[2][BK * RB2];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
 
   const int num_qtiles = (int)((p.NQ + BQ - 1) / BQ);

@@ -21,12 +21,14 @@
 // whole key loop; K tiles are loaded straight into LDS (direct-to-LDS loads,
 // XOR-swizzled rows for conflict-free 16-byte reads), shared by the 4 waves and
 // double-buffered: the loads of the next tile are issued before the current
-// one is computed.  The online update
-// runs per 32-key block (one max, two correction factors per block and row).
+// one is computed.  The online update runs per 32-key block (one max, two
+// correction factors per block and row), one block behind the MFMAs.
 //
 // Split-K (article section "GPU kernel optimisations"): the same kernel over a
 // contiguous key range writes the five per-row partials (m1, l1, m2, l2, acc)
 // instead of the final values; reduce_kernel merges them.
+
+#include <type_traits>
 
 #include "skl_device.h"
 #include "skl_internal.h"
@@ -48,7 +50,8 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(c
   __shared__ __attribute__((aligned(1024))) char sK2[2][BK * RB2];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int half = lane >> 5, col = lane & 31;
 
   // Tile decode: logical tile -> (bh, query tile[, split]).
@@ -106,81 +109,120 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(c
   wait_vm();
   __syncthreads();
 
-  for (int64_t it = 0; it < nsteps; ++it) {
-    const int st = (int)(it & 1);
-    const int64_t j0 = kbeg + it * BK;
-    if (it + 1 < nsteps) fetch(st ^ 1, j0 + BK);
+  // Per-lane byte offsets of the A fragments inside a 32-row block: the
+  // swizzle repeats every 16 rows, so block kb of stage st is at the constant
+  // st * BK * RB + kb * 32 * RB from these (an immediate of the LDS read).
+  int aoff1[NC1], aoff2[NC2];
+#pragma unroll
+  for (int c = 0; c < NC1; ++c) aoff1[c] = T1::off(col, (c * KC + half * EPL) * ESZ);
+#pragma unroll
+  for (int c = 0; c < NC2; ++c) aoff2[c] = T2::off(col, (c * KC + half * EPL) * ESZ);
 
-    if (j0 <= wave_kmax) {
-#pragma unroll
-      for (int kb = 0; kb < BK / 32; ++kb) {
-        const int64_t jb = j0 + kb * 32;
-        if (jb > wave_kmax) break;  // the rest of the tile is masked for this wave
-        f32x16 s1 = f32x16{}, s2 = f32x16{};
-        const int krow = kb * 32 + col;
-#pragma unroll
-        for (int c = 0; c < NC1; ++c)
-          s1 = M::run(M::load(&sK1[st][T1::off(krow, (c * KC + half * EPL) * ESZ)]), qf1[c], s1);
-#pragma unroll
-        for (int c = 0; c < NC2; ++c)
-          s2 = M::run(M::load(&sK2[st][T2::off(krow, (c * KC + half * EPL) * ESZ)]), qf2[c], s2);
+  static_assert(BK == 64, "the block pipeline below assumes two 32-key blocks per tile");
 
-        const bool need_mask = (jb + 32 > p.NK) || (CAUSAL && jb + 31 > qw0 + off);
-        if (need_mask) {
-          // Key jb + ro is visible iff ro < NK - jb and (causal) ro <= qi + off - jb.
-          const int klim = clamp_i32(p.NK - jb), cmax = clamp_i32(qi + off - jb);
+  // Logits of 32-key block kb of ring stage ST: all A fragments are read
+  // first, then the two MFMA chains are interleaved.
+  auto logits = [&](auto stc, int kb, f32x16& s1, f32x16& s2) {
+    constexpr int st = decltype(stc)::value;
+    frag ka1[NC1], ka2[NC2];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int ro = acc_row(r, half);
-            if (!(ro < klim && (!CAUSAL || ro <= cmax))) {
-              s1[r] = neg_inf();
-              s2[r] = neg_inf();
-            }
-          }
+    for (int c = 0; c < NC1; ++c) ka1[c] = M::load(&sK1[st][kb * 32 * RB1 + aoff1[c]]);
+#pragma unroll
+    for (int c = 0; c < NC2; ++c) ka2[c] = M::load(&sK2[st][kb * 32 * RB2 + aoff2[c]]);
+    s1 = f32x16{};
+    s2 = f32x16{};
+#pragma unroll
+    for (int c = 0; c < (NC1 > NC2 ? NC1 : NC2); ++c) {
+      if (c < NC1) s1 = M::run(ka1[c], qf1[c], s1);
+      if (c < NC2) s2 = M::run(ka2[c], qf2[c], s2);
+    }
+  };
+
+  // Online update of the row statistics with one block whose first key is jb.
+  auto update = [&](f32x16& s1, f32x16& s2, int64_t jb) {
+    const bool need_mask = (jb + 32 > p.NK) || (CAUSAL && jb + 31 > qw0 + off);
+    if (need_mask) {
+      // Key jb + ro is visible iff ro < NK - jb and (causal) ro <= qi + off - jb.
+      const int klim = clamp_i32(p.NK - jb), cmax = clamp_i32(qi + off - jb);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ro = acc_row(r, half);
+        if (!(ro < klim && (!CAUSAL || ro <= cmax))) {
+          s1[r] = neg_inf();
+          s2[r] = neg_inf();
         }
-
-        float mx1 = neg_inf(), mx2 = neg_inf();
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          mx1 = fmaxf(mx1, s1[r]);
-          mx2 = fmaxf(mx2, s2[r]);
-        }
-        const float m1n = fmaxf(m1, mx1 * c1), m2n = fmaxf(m2, mx2 * c2);
-        const float m1u = (m1n == neg_inf()) ? 0.f : m1n;  // no key seen yet: keep sums at 0
-        const float m2u = (m2n == neg_inf()) ? 0.f : m2n;
-        const float a1f = exp2_hw(m1 - m1u), a2f = exp2_hw(m2 - m2u);
-
-        float sum1 = 0.f, sum2 = 0.f, accd = 0.f;
-        if (need_mask) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float u1 = fmaf(s1[r], c1, -m1u), u2 = fmaf(s2[r], c2, -m2u);
-            const float e1 = exp2_hw(u1), e2 = exp2_hw(u2);
-            sum1 += e1;
-            sum2 += e2;
-            const float d = (s1[r] == neg_inf()) ? 0.f : (u1 - u2);
-            accd = fmaf(e1, d, accd);
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float u1 = fmaf(s1[r], c1, -m1u), u2 = fmaf(s2[r], c2, -m2u);
-            const float e1 = exp2_hw(u1), e2 = exp2_hw(u2);
-            sum1 += e1;
-            sum2 += e2;
-            accd = fmaf(e1, u1 - u2, accd);
-          }
-        }
-        // t1 - t2 = (u1 - u2) + (m1u - m2u): the per-row part is added once per block.
-        l1 = fmaf(l1, a1f, sum1);
-        l2 = fmaf(l2, a2f, sum2);
-        acc = fmaf(acc, a1f, fmaf(m1u - m2u, sum1, accd));
-        m1 = m1n;
-        m2 = m2n;
       }
     }
+
+    // Reductions over the 16 values run as 4 independent chains (and a tree
+    // for the max): with two waves per SIMD a single dependent chain of 16
+    // would leave the VALU waiting on its own latency.
+    float px1[4], px2[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      px1[k] = fmaxf(fmaxf(s1[4 * k], s1[4 * k + 1]), fmaxf(s1[4 * k + 2], s1[4 * k + 3]));
+      px2[k] = fmaxf(fmaxf(s2[4 * k], s2[4 * k + 1]), fmaxf(s2[4 * k + 2], s2[4 * k + 3]));
+    }
+    const float mx1 = fmaxf(fmaxf(px1[0], px1[1]), fmaxf(px1[2], px1[3]));
+    const float mx2 = fmaxf(fmaxf(px2[0], px2[1]), fmaxf(px2[2], px2[3]));
+    const float m1n = fmaxf(m1, mx1 * c1), m2n = fmaxf(m2, mx2 * c2);
+    const float m1u = (m1n == neg_inf()) ? 0.f : m1n;  // no key seen yet: keep sums at 0
+    const float m2u = (m2n == neg_inf()) ? 0.f : m2n;
+    const float a1f = exp2_hw(m1 - m1u), a2f = exp2_hw(m2 - m2u);
+
+    float ps1[4] = {0.f, 0.f, 0.f, 0.f}, ps2[4] = {0.f, 0.f, 0.f, 0.f}, pa[4] = {0.f, 0.f, 0.f, 0.f};
+    if (need_mask) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float u1 = fmaf(s1[r], c1, -m1u), u2 = fmaf(s2[r], c2, -m2u);
+        const float e1 = exp2_hw(u1), e2 = exp2_hw(u2);
+        ps1[r & 3] += e1;
+        ps2[r & 3] += e2;
+        const float d = (s1[r] == neg_inf()) ? 0.f : (u1 - u2);
+        pa[r & 3] = fmaf(e1, d, pa[r & 3]);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float u1 = fmaf(s1[r], c1, -m1u), u2 = fmaf(s2[r], c2, -m2u);
+        const float e1 = exp2_hw(u1), e2 = exp2_hw(u2);
+        ps1[r & 3] += e1;
+        ps2[r & 3] += e2;
+        pa[r & 3] = fmaf(e1, u1 - u2, pa[r & 3]);
+      }
+    }
+    const float sum1 = (ps1[0] + ps1[1]) + (ps1[2] + ps1[3]);
+    const float sum2 = (ps2[0] + ps2[1]) + (ps2[2] + ps2[3]);
+    const float accd = (pa[0] + pa[1]) + (pa[2] + pa[3]);
+    // t1 - t2 = (u1 - u2) + (m1u - m2u): the per-row part is added once per block.
+    l1 = fmaf(l1, a1f, sum1);
+    l2 = fmaf(l2, a2f, sum2);
+    acc = fmaf(acc, a1f, fmaf(m1u - m2u, sum1, accd));
+    m1 = m1n;
+    m2 = m2n;
+  };
+
+  // Block-level software pipeline: the MFMAs of the next 32-key block are
+  // issued before the online update of the current one (across the tile
+  // barrier too), so each wave keeps matrix work in flight while its VALU
+  // runs the softmax.  Blocks past the wave's last visible key are skipped.
+  f32x16 sa1, sa2, sb1, sb2;  // block 0 / block 1 of the current tile
+  auto step = [&](auto stc, int64_t it) {
+    constexpr int st = decltype(stc)::value;
+    const int64_t j0 = kbeg + it * BK;
+    if (it + 1 < nsteps) fetch(st ^ 1, j0 + BK);
+    const bool live0 = j0 <= wave_kmax, live1 = j0 + 32 <= wave_kmax;
+    if (live1) logits(stc, 1, sb1, sb2);
+    if (live0) update(sa1, sa2, j0);
     wait_vm();
     __syncthreads();
+    if (it + 1 < nsteps && j0 + BK <= wave_kmax) logits(std::integral_constant<int, st ^ 1>{}, 0, sa1, sa2);
+    if (live1) update(sb1, sb2, j0 + 32);
+  };
+  if (nsteps > 0 && kbeg <= wave_kmax) logits(std::integral_constant<int, 0>{}, 0, sa1, sa2);
+  for (int64_t it = 0; it < nsteps; it += 2) {
+    step(std::integral_constant<int, 0>{}, it);
+    if (it + 1 < nsteps) step(std::integral_constant<int, 1>{}, it + 1);
   }
 
   // Merge the two lane halves (disjoint key subsets of the same row).
