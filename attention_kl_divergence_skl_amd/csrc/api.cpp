@@ -83,6 +83,11 @@ skl_status check_shape(const skl_shape* s, bool need_nk) {
         return fail(SKL_ERR_UNSUPPORTED, "stride %lld not a multiple of %lld elements", (long long)all[t][a],
                     (long long)mult);
     }
+  // Tile loads address a 64-row span with 32-bit offsets.
+  const int64_t esz = s->dtype == SKL_BF16 ? 2 : 4;
+  for (int t = 0; t < 4; ++t)
+    if (all[t][2] * esz * 64 >= (int64_t(1) << 31))
+      return fail(SKL_ERR_UNSUPPORTED, "row stride %lld elements too large", (long long)all[t][2]);
   return ok();
 }
 

@@ -123,16 +123,19 @@ __device__ __forceinline__ void tile_load_async(char* tile, const char* g, int64
   constexpr int RPI = 1024 / ROWB;      // rows per wave instruction
   constexpr int NI = ROWS / RPI;        // instructions per tile
   static_assert(NI % 4 == 0, "tile must split evenly over 4 waves");
+  // Uniform 64-bit row base plus a 32-bit per-lane offset (the host keeps
+  // ROWS * rs below 2^31).
+  const char* const base = g + j0 * rs;
+  const int rmax = (int)(nrows - 1 - j0 < ROWS - 1 ? nrows - 1 - j0 : ROWS - 1);
   const int pc = lane % TL::CPR;
+  const int irs = (int)rs;
 #pragma unroll
   for (int k = 0; k < NI / 4; ++k) {
     const int m = wave + 4 * k;
     const int r = m * RPI + lane / TL::CPR;
     const int lc = pc ^ TL::swz(r);
-    int64_t gr = j0 + r;
-    gr = gr < nrows ? gr : nrows - 1;
-    const char* src = g + gr * rs + lc * 16;
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+    const int rr = r < rmax ? r : rmax;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(base + (rr * irs + lc * 16)),
                                      (__attribute__((address_space(3))) void*)(tile + m * 1024), 16, 0, 0);
   }
 }
