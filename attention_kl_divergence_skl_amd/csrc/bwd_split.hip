@@ -141,6 +141,10 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dk_kerne
   __syncthreads();
   const float c1 = p.c1, c2 = p.c2;
   const int prow = rperm(col);
+  // LDS address bases (bf16 tiles; unused by the fp32 instantiations).
+  const SwzAddr<RB1> ad1(prow, half, lane);
+  const SwzAddr<RB2> ad2(prow, half, lane);
+  const SwzAddr<RBG> adg(prow, half, lane);
 
   for (int64_t it = 0; it < nsteps; ++it) {
     const int st = (int)(it & 1);
@@ -153,13 +157,20 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dk_kerne
       const int64_t qb0 = q0 + 32 * qb;
       if (kw0 >= p.NK || qb0 >= p.NQ || (CAUSAL && kw0 > qb0 + 31 + off)) continue;  // block fully masked
       f32x16 s1 = f32x16{}, s2 = f32x16{};
-      const int qrow = 32 * qb + prow;
+      if constexpr (EPL == 1) {
+        const int qrow = 32 * qb + prow;
 #pragma unroll
-      for (int c = 0; c < NC1; ++c)
-        s1 = M::run(M::load(&sQ1[st][T1::off(qrow, (c * KC + half * EPL) * ESZ)]), kf1[c], s1);
+        for (int c = 0; c < NC1; ++c)
+          s1 = M::run(M::load(&sQ1[st][T1::off(qrow, (c * KC + half * EPL) * ESZ)]), kf1[c], s1);
 #pragma unroll
-      for (int c = 0; c < NC2; ++c)
-        s2 = M::run(M::load(&sQ2[st][T2::off(qrow, (c * KC + half * EPL) * ESZ)]), kf2[c], s2);
+        for (int c = 0; c < NC2; ++c)
+          s2 = M::run(M::load(&sQ2[st][T2::off(qrow, (c * KC + half * EPL) * ESZ)]), kf2[c], s2);
+      } else {
+#pragma unroll
+        for (int c = 0; c < NC1; ++c) s1 = M::run(ad1.frag(sQ1[st], 32 * qb * RB1, c), kf1[c], s1);
+#pragma unroll
+        for (int c = 0; c < NC2; ++c) s2 = M::run(ad2.frag(sQ2[st], 32 * qb * RB2, c), kf2[c], s2);
+      }
 
       // Registers 8 run .. 8 run + 7 hold rows 32 qb + 16 run + 8 half + 0..7:
       // their row constants are two float4 reads, and they form K chunk
@@ -204,7 +215,7 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dk_kerne
 #pragma unroll
           for (int e = 0; e < EPL; ++e) a[e] = from_f32<T>(ds[e]);
 #pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) dk[cb] = M::run(a, lds_tr_frag_swz<RBG>(qg, 32 * qb + run * KC, 32 * cb, lane), dk[cb]);
+          for (int cb = 0; cb < NCB; ++cb) dk[cb] = M::run(a, adg.trfrag(qg, (32 * qb + run * KC) * RBG, cb), dk[cb]);
         }
       }
     }

@@ -144,6 +144,48 @@ __device__ __forceinline__ void tile_load_async(char* tile, const char* g, int64
 // ones) have landed: s_waitcnt vmcnt(0).
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// a ^ b evaluated where it is written.  The volatile asm keeps the compiler
+// from hoisting per-chunk LDS addresses out of a loop as invariants (each
+// would hold a VGPR for the whole loop); b is a constant kept in an SGPR.
+__device__ __forceinline__ int xor_here(int a, int b) {
+  int r;
+  asm volatile("v_xor_b32 %0, %1, %2" : "=v"(r) : "s"(b), "v"(a));
+  return r;
+}
+
+// Per-lane parts of the LDS addresses of a bf16 SwzTile (ROWB = 128 or 256).
+// The chunk XOR and the row base never share bits, so every address is
+// (one per-lane base) ^ (a chunk constant) + (a block/stage constant).
+template <int ROWB>
+struct SwzAddr {
+  using TL = SwzTile<ROWB>;
+  int afrag;     // A/B-operand fragment of row `r`: offset of chunk 2c + half is afrag ^ (c << 5)
+  int tr[2];     // transposing read t: offset for column block cb is tr[t] ^ (cb << 6)
+  __device__ __forceinline__ SwzAddr(int r, int half, int lane) {
+    afrag = r * ROWB + ((half ^ TL::swz(r)) << 4);
+    const int g = lane >> 4, L = lane & 15;
+    const int cl = 2 * (g & 1) + ((L & 3) >> 1);  // chunk within a 32-column block
+    const int lo = 8 * (L & 1);                   // byte within the chunk
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int row = 8 * (g >> 1) + (L >> 2) + 4 * t;
+      tr[t] = row * ROWB + ((cl ^ TL::swz(row)) << 4) + lo;
+    }
+  }
+  // 16-byte A/B fragment, K chunk c, of rows starting at block base `blk` (bytes, multiple of 16 rows).
+  __device__ __forceinline__ bf16x8 frag(const char* tile, int blk, int c) const {
+    return *reinterpret_cast<const bf16x8*>(tile + blk + xor_here(afrag, c << 5));
+  }
+  // Transposing-read operand (rows k0.. of the tile = blk, columns 32 cb ..).
+  __device__ __forceinline__ bf16x8 trfrag(const char* tile, int blk, int cb) const {
+    const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + blk + xor_here(tr[0], cb << 6)));
+    const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + blk + xor_here(tr[1], cb << 6)));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 v = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  }
+};
+
 // Transposing-read operand (see lds_tr_frag) from a SwzTile of bf16 rows.
 template <int ROWB>
 __device__ __forceinline__ bf16x8 lds_tr_frag_swz(const char* tile, int k0, int n0, int lane) {
