@@ -30,6 +30,14 @@ HIPCC_FLAGS = [
     "-I", os.path.join(ROOT, "include"),
 ]
 
+# Per-source additions.  The forward's running max is an fmaxf tree over MFMA
+# results; under IEEE NaN semantics every operand is first quieted with an
+# extra v_max_f32 (one VALU op per logit, about a sixth of the kernel's VALU
+# work).  The forward never produces a NaN that it consumes (masked logits are
+# -inf and are selected away before any inf - inf is used; an all-masked row
+# works with m = 0), so it is compiled without NaN semantics.
+SOURCE_FLAGS = {"fwd.hip": ["-fno-honor-nans"]}
+
 
 def _hipcc() -> str:
     for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
@@ -41,7 +49,8 @@ def _hipcc() -> str:
 def _compile(src: str, extra) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [_hipcc()] + HIPCC_FLAGS + list(extra) + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc()] + HIPCC_FLAGS + SOURCE_FLAGS.get(src, []) + list(extra) + lang
+    cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")

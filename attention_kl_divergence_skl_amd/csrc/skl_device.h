@@ -135,7 +135,8 @@ __device__ __forceinline__ void tile_load_async(char* tile, const char* g, int64
     const int r = m * RPI + lane / TL::CPR;
     const int lc = pc ^ TL::swz(r);
     const int rr = r < rmax ? r : rmax;
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(base + (rr * irs + lc * 16)),
+    const unsigned off = (unsigned)(rr * irs + lc * 16);  // non-negative: scalar-base addressing
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(base + off),
                                      (__attribute__((address_space(3))) void*)(tile + m * 1024), 16, 0, 0);
   }
 }

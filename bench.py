@@ -45,8 +45,10 @@ def log(msg: str) -> None:
 
 def source_sha(kernel: str) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, "attention_kl_divergence_skl_amd", "csrc", f), "rb") as fh:
+    pkg = os.path.join(ROOT, "attention_kl_divergence_skl_amd")
+    # the build script carries per-source compiler flags, so it is hashed too
+    for path in [os.path.join(pkg, "csrc", f) for f in KERNEL_SOURCES[kernel]] + [os.path.join(pkg, "build.py")]:
+        with open(path, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
