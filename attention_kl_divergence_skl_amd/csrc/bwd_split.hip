@@ -176,6 +176,11 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dk_kerne
       // their row constants are two float4 reads, and they form K chunk
       // `run` (bf16) or chunks 8 run .. 8 run + 7 (fp32) of dK += dSᵀ Q_g, so
       // each run is converted and consumed right away.
+      // The mask is applied in one pass per run of 8 registers, after dS.
+      // (need_mask is uniform over the wave, but stating that here -- as the
+      // dQ kernel does -- splits the block into scalar branches and makes this
+      // kernel spill; as a per-lane condition it costs one exec-mask region
+      // per run.)
       const bool need_mask = (qb0 + 32 > p.NQ) || (kw0 + 32 > p.NK) || (CAUSAL && kw0 + 31 > qb0 + off);
       // Row qb0 + ro sees this lane's key iff ro < NQ - qb0 and (causal) ro >= key - qb0 - off.
       const int qlim = clamp_i32(p.NQ - qb0), cmin = clamp_i32(key - qb0 - off);
@@ -193,12 +198,14 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dk_kerne
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int r = 8 * run + i;
-          float v = dS_of<TEACHER>(s1[r], s2[r], c1, c2, cst[0][i], cst[1][i], cst[2][i], TEACHER ? cst[3][i] : 0.f);
-          if (need_mask) {
-            const int ro = rloc(r, half);
-            v = (kvalid && ro < qlim && (!CAUSAL || ro >= cmin)) ? v : 0.f;
+          ds[i] = dS_of<TEACHER>(s1[r], s2[r], c1, c2, cst[0][i], cst[1][i], cst[2][i], TEACHER ? cst[3][i] : 0.f);
+        }
+        if (need_mask) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int ro = rloc(8 * run + i, half);
+            ds[i] = (kvalid && ro < qlim && (!CAUSAL || ro >= cmin)) ? ds[i] : 0.f;
           }
-          ds[i] = v;
         }
         if constexpr (EPL == 1) {
 #pragma unroll
@@ -326,8 +333,8 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kerne
     const int64_t j0 = it * BK;
     if (it + 1 < nsteps) fetch(st ^ 1, j0 + BK);
 
-    if (j0 <= wave_kmax) {
-      const bool need_mask = (j0 + BK > p.NK) || (CAUSAL && j0 + BK - 1 > qw0 + off) || (qw0 + 32 > p.NQ);
+    if (wave_uniform(j0 <= wave_kmax)) {
+      const bool need_mask = wave_uniform((j0 + BK > p.NK) || (CAUSAL && j0 + BK - 1 > qw0 + off) || (qw0 + 32 > p.NQ));
       const char* kg = TEACHER ? &sK1[st][0] : &sK2[st][0];
 #pragma unroll
       for (int kb = 0; kb < BK / 32; ++kb) {
@@ -350,12 +357,14 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kerne
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             const int r = 8 * run + i;
-            float v = dS_of<TEACHER>(s1[r], s2[r], c1, c2, L1, L2, ga, gb);
-            if (need_mask) {
-              const int ro = rloc(r, half);
-              v = (qvalid && ro < klim && (!CAUSAL || ro <= cmax)) ? v : 0.f;
+            ds[i] = dS_of<TEACHER>(s1[r], s2[r], c1, c2, L1, L2, ga, gb);
+          }
+          if (need_mask) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const int ro = rloc(8 * run + i, half);
+              ds[i] = (qvalid && ro < klim && (!CAUSAL || ro <= cmax)) ? ds[i] : 0.f;
             }
-            ds[i] = v;
           }
           if constexpr (EPL == 1) {
 #pragma unroll

@@ -141,6 +141,12 @@ __device__ __forceinline__ void tile_load_async(char* tile, const char* g, int64
   }
 }
 
+// A condition that has the same value in every lane of the wave, made visibly
+// uniform: branches on it become scalar branches instead of per-lane
+// predication (the compiler cannot tell that values derived from tid >> 6 are
+// uniform).
+__device__ __forceinline__ bool wave_uniform(bool c) { return __builtin_amdgcn_readfirstlane((int)c) != 0; }
+
 // Wait until this wave's outstanding global loads (including direct-to-LDS
 // ones) have landed: s_waitcnt vmcnt(0).
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
