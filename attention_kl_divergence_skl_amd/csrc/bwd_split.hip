@@ -22,6 +22,8 @@
 // LDS tile through gfx950 transposing reads (lds_tr_frag), so no transposed
 // copy of anything is ever written.
 
+#include <type_traits>
+
 #include "skl_device.h"
 #include "skl_internal.h"
 
@@ -146,17 +148,28 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dk_kerne
   const SwzAddr<RB2> ad2(prow, half, lane);
   const SwzAddr<RBG> adg(prow, half, lane);
 
-  for (int64_t it = 0; it < nsteps; ++it) {
+  // One query step.  The stage (which LDS buffer) is a template constant so
+  // the buffer address folds into the immediate offset of every LDS read;
+  // MASKED steps are those whose 64 x 128 (query, key) rectangle reaches past
+  // the causal diagonal or a ragged edge, decided from workgroup-uniform
+  // values, so the common unmasked step carries no mask code at all.
+  auto step = [&](auto masked, int64_t it) __attribute__((always_inline)) {
     const int st = (int)(it & 1);
+    constexpr bool MASKED = decltype(masked)::value;
     const int64_t q0 = qbeg + it * BQ;
     if (it + 1 < nsteps) fetch(st ^ 1, q0 + BQ);  // next tile in flight during this step
 
-    const char* qg = TEACHER ? &sQ1[st][0] : &sQ2[st][0];
+    const char* qg = TEACHER ? &sQ1[0][0] : &sQ2[0][0];  // addressed through xg below (bf16) ...
+    const char* qgs = TEACHER ? &sQ1[st][0] : &sQ2[st][0];  // ... or directly (fp32)
+    const SwzAddr<RB1> x1 = ad1.shifted(st * BQ * RB1);
+    const SwzAddr<RB2> x2 = ad2.shifted(st * BQ * RB2);
+    const SwzAddr<RBG> xg = adg.shifted(st * BQ * RBG);
 #pragma unroll
     for (int qb = 0; qb < BQ / 32; ++qb) {
       const int64_t qb0 = q0 + 32 * qb;
-      if (kw0 >= p.NK || qb0 >= p.NQ || (CAUSAL && kw0 > qb0 + 31 + off)) continue;  // block fully masked
+      if (MASKED && (kw0 >= p.NK || qb0 >= p.NQ || (CAUSAL && kw0 > qb0 + 31 + off))) continue;  // fully masked
       f32x16 s1 = f32x16{}, s2 = f32x16{};
+      __builtin_amdgcn_s_setprio(1);  // MFMA burst at raised priority (as in the forward)
       if constexpr (EPL == 1) {
         const int qrow = 32 * qb + prow;
 #pragma unroll
@@ -167,21 +180,19 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dk_kerne
           s2 = M::run(M::load(&sQ2[st][T2::off(qrow, (c * KC + half * EPL) * ESZ)]), kf2[c], s2);
       } else {
 #pragma unroll
-        for (int c = 0; c < NC1; ++c) s1 = M::run(ad1.frag(sQ1[st], 32 * qb * RB1, c), kf1[c], s1);
+        for (int c = 0; c < NC1; ++c) s1 = M::run(x1.frag(sQ1[0], 32 * qb * RB1, c), kf1[c], s1);
 #pragma unroll
-        for (int c = 0; c < NC2; ++c) s2 = M::run(ad2.frag(sQ2[st], 32 * qb * RB2, c), kf2[c], s2);
+        for (int c = 0; c < NC2; ++c) s2 = M::run(x2.frag(sQ2[0], 32 * qb * RB2, c), kf2[c], s2);
       }
 
+      __builtin_amdgcn_s_setprio(0);
       // Registers 8 run .. 8 run + 7 hold rows 32 qb + 16 run + 8 half + 0..7:
       // their row constants are two float4 reads, and they form K chunk
       // `run` (bf16) or chunks 8 run .. 8 run + 7 (fp32) of dK += dSᵀ Q_g, so
       // each run is converted and consumed right away.
-      // The mask is applied in one pass per run of 8 registers, after dS.
-      // (need_mask is uniform over the wave, but stating that here -- as the
-      // dQ kernel does -- splits the block into scalar branches and makes this
-      // kernel spill; as a per-lane condition it costs one exec-mask region
-      // per run.)
-      const bool need_mask = (qb0 + 32 > p.NQ) || (kw0 + 32 > p.NK) || (CAUSAL && kw0 + 31 > qb0 + off);
+      // Within a masked step the mask is applied in one pass per run of 8
+      // registers, under a per-lane condition (one exec-mask region per run).
+      const bool need_mask = MASKED && ((qb0 + 32 > p.NQ) || (kw0 + 32 > p.NK) || (CAUSAL && kw0 + 31 > qb0 + off));
       // Row qb0 + ro sees this lane's key iff ro < NQ - qb0 and (causal) ro >= key - qb0 - off.
       const int qlim = clamp_i32(p.NQ - qb0), cmin = clamp_i32(key - qb0 - off);
 #pragma unroll
@@ -213,7 +224,7 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dk_kerne
             const int c = 8 * run + i;
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
-              const float bq = *reinterpret_cast<const float*>(qg + TG::off(32 * qb + rloc(c, half), (32 * cb + col) * ESZ));
+              const float bq = *reinterpret_cast<const float*>(qgs + TG::off(32 * qb + rloc(c, half), (32 * cb + col) * ESZ));
               dk[cb] = M::run(ds[i], bq, dk[cb]);
             }
           }
@@ -222,14 +233,29 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dk_kerne
 #pragma unroll
           for (int e = 0; e < EPL; ++e) a[e] = from_f32<T>(ds[e]);
 #pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) dk[cb] = M::run(a, adg.trfrag(qg, (32 * qb + run * KC) * RBG, cb), dk[cb]);
+          for (int cb = 0; cb < NCB; ++cb) dk[cb] = M::run(a, xg.trfrag(qg, (32 * qb + run * KC) * RBG, cb), dk[cb]);
         }
       }
     }
     if (it + 1 < nsteps) stash(st ^ 1);
     wait_vm();
     __syncthreads();
+  };
+  // Steps [0, head) reach the causal diagonal, [tail, nsteps) the ragged
+  // query edge; a ragged key tile masks every step.
+  int64_t head = 0, tail = nsteps;
+  if (kt0 + kBwdBK > p.NK) {
+    head = nsteps;
+  } else {
+    // step it is masked iff qbeg + it BQ < kt0 + kBwdBK - 1 - off =: x
+    const int64_t x = kt0 + kBwdBK - 1 - off - qbeg;
+    if (CAUSAL && x > 0) head = min(nsteps, (x + BQ - 1) / BQ);
+    if (p.NQ % BQ != 0) tail = max(head, nsteps - 1);
   }
+  int64_t it = 0;
+  for (; it < head; ++it) step(std::true_type{}, it);
+  for (; it < tail; ++it) step(std::false_type{}, it);
+  for (; it < nsteps; ++it) step(std::true_type{}, it);
 
   char* const dkp = (char*)p.dk + (b * p.sdk.b + h * p.sdk.h) * ESZ;
 #pragma unroll
@@ -328,26 +354,35 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kerne
   const float c1 = p.c1, c2 = p.c2;
   const int prow = rperm(col);
 
-  for (int64_t it = 0; it < nsteps; ++it) {
+  // One key step (64 keys).  MASKED steps are those that reach the causal
+  // diagonal of some wave or a ragged edge; the others carry no mask code.
+  auto step = [&](auto masked, int64_t it) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked)::value;
     const int st = (int)(it & 1);
     const int64_t j0 = it * BK;
     if (it + 1 < nsteps) fetch(st ^ 1, j0 + BK);
 
-    if (wave_uniform(j0 <= wave_kmax)) {
-      const bool need_mask = wave_uniform((j0 + BK > p.NK) || (CAUSAL && j0 + BK - 1 > qw0 + off) || (qw0 + 32 > p.NQ));
+    if (!MASKED || wave_uniform(j0 <= wave_kmax)) {
+      const bool need_mask =
+          MASKED && wave_uniform((j0 + BK > p.NK) || (CAUSAL && j0 + BK - 1 > qw0 + off) || (qw0 + 32 > p.NQ));
+      // (Here the per-chunk LDS offsets are left to the compiler, which keeps
+      // them as loop invariants: measured faster than forming them at each
+      // read as the dK kernel does.)
       const char* kg = TEACHER ? &sK1[st][0] : &sK2[st][0];
 #pragma unroll
       for (int kb = 0; kb < BK / 32; ++kb) {
         f32x16 s1 = f32x16{}, s2 = f32x16{};
-        const int krow = kb * 32 + prow;
+        __builtin_amdgcn_s_setprio(1);  // MFMA burst at raised priority (as in the forward)
         // Key j0 + 32 kb + ro is visible iff ro < NK - jb and (causal) ro <= qi + off - jb.
         const int klim = clamp_i32(p.NK - (j0 + kb * 32)), cmax = clamp_i32(qi + off - (j0 + kb * 32));
+        const int krow = kb * 32 + prow;
 #pragma unroll
         for (int c = 0; c < NC1; ++c)
           s1 = M::run(M::load(&sK1[st][T1::off(krow, (c * KC + half * EPL) * ESZ)]), qf1[c], s1);
 #pragma unroll
         for (int c = 0; c < NC2; ++c)
           s2 = M::run(M::load(&sK2[st][T2::off(krow, (c * KC + half * EPL) * ESZ)]), qf2[c], s2);
+        __builtin_amdgcn_s_setprio(0);
         // Registers 8 run .. 8 run + 7 hold keys kb 32 + 16 run + 8 half + 0..7:
         // K chunk `run` (bf16) or chunks 8 run .. 8 run + 7 (fp32) of
         // dQ += dS K_g, consumed as soon as they are formed.
@@ -381,15 +416,28 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kerne
 #pragma unroll
             for (int e = 0; e < EPL; ++e) a[e] = from_f32<T>(ds[e]);
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb)
-              dq[cb] = M::run(a, lds_tr_frag_swz<RBG>(kg, kb * 32 + run * KC, 32 * cb, lane), dq[cb]);
+            for (int cb = 0; cb < NCB; ++cb) dq[cb] = M::run(a, lds_tr_frag_swz<RBG>(kg, kb * 32 + run * KC, 32 * cb, lane), dq[cb]);
           }
         }
       }
     }
     wait_vm();
     __syncthreads();
+  };
+  // Steps [tail, nsteps) reach the causal diagonal of some wave (keys past
+  // qt 128 + off - 63) or the ragged key edge; a ragged query tile masks all.
+  int64_t tail = 0;
+  if ((int64_t)qt * BQ + BQ <= p.NQ) {
+    tail = nsteps;
+    if (p.NK % BK != 0) tail = nsteps - 1;
+    // step it is masked iff it BK >= qt BQ + off - BK + 2 =: y
+    const int64_t y = (int64_t)qt * BQ + off - BK + 2;
+    if (CAUSAL) tail = min(tail, y > 0 ? (y + BK - 1) / BK : (int64_t)0);
+    tail = max(tail, (int64_t)0);
   }
+  int64_t it = 0;
+  for (; it < tail; ++it) step(std::false_type{}, it);
+  for (; it < nsteps; ++it) step(std::true_type{}, it);
 
   // dQ of this wave's rows: accumulator register r holds query qw0 + acc_row(r, half).
   char* const dqp = (char*)p.dq + (b * p.sdq.b + h * p.sdq.h) * ESZ;

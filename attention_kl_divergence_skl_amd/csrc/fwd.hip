@@ -131,11 +131,16 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(c
     for (int c = 0; c < NC2; ++c) ka2[c] = M::load(&sK2[st][kb * 32 * RB2 + aoff2[c]]);
     s1 = f32x16{};
     s2 = f32x16{};
+    // Raised wave priority while the MFMAs issue: the other wave of the SIMD,
+    // in its VALU phase, then fills the gaps instead of competing for issue,
+    // which keeps the two waves out of phase.
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int c = 0; c < (NC1 > NC2 ? NC1 : NC2); ++c) {
       if (c < NC1) s1 = M::run(ka1[c], qf1[c], s1);
       if (c < NC2) s2 = M::run(ka2[c], qf2[c], s2);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // Online update of the row statistics with one block whose first key is jb.

@@ -179,6 +179,17 @@ struct SwzAddr {
       tr[t] = row * ROWB + ((cl ^ TL::swz(row)) << 4) + lo;
     }
   }
+  // The same addresses in a buffer `bytes` further on (a multiple of 1024, so
+  // it commutes with the chunk XOR).  Taking the stage of a double buffer into
+  // the per-lane base once per step leaves only constants to be added at each
+  // read, which the LDS instructions take as immediate offsets.
+  __device__ __forceinline__ SwzAddr shifted(int bytes) const {
+    SwzAddr o = *this;
+    o.afrag += bytes;
+    o.tr[0] += bytes;
+    o.tr[1] += bytes;
+    return o;
+  }
   // 16-byte A/B fragment, K chunk c, of rows starting at block base `blk` (bytes, multiple of 16 rows).
   __device__ __forceinline__ bf16x8 frag(const char* tile, int blk, int c) const {
     return *reinterpret_cast<const bf16x8*>(tile + blk + xor_here(afrag, c << 5));
