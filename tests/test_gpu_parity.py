@@ -39,6 +39,14 @@ CASES = [
     W("bf16_single_row", 1, 1, 1, 1, 128, 128, "bf16", True),
     W("bf16_one_query_many_keys", 1, 1, 1, 517, 128, 64, "bf16", False),
     W("bf16_n17", 1, 3, 17, 17, 128, 128, "bf16", True),
+    # Tile-aligned and half-aligned shapes: the backward separates the steps
+    # that reach the causal diagonal or a ragged edge from mask-free ones, so
+    # these pin each combination of aligned / ragged N_Q and N_K.
+    W("bf16_aligned_causal", 1, 2, 512, 512, 128, 128, "bf16", True, synth.Recipe("corr", noise=0.3)),
+    W("f32_aligned_causal", 1, 1, 384, 384, 64, 64, "f32", True),
+    W("bf16_nq_aligned_nk_ragged_causal", 1, 2, 256, 333, 128, 128, "bf16", True),
+    W("bf16_nq_ragged_nk_aligned_causal", 1, 2, 200, 512, 128, 64, "bf16", True),
+    W("bf16_nq_aligned_nk_ragged_noncausal", 1, 2, 384, 200, 64, 128, "bf16", False),
 ]
 
 
