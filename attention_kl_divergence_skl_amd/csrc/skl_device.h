@@ -90,17 +90,23 @@ __device__ __forceinline__ bf16x8 lds_tr_frag(const char* tile, int pitch, int k
 
 // A tile of row-major rows held in LDS with no padding: row r occupies
 // [r * ROWB, (r + 1) * ROWB) and its 16-byte chunks are permuted by
-// chunk' = chunk ^ swz(r).  The permutation makes the two read patterns of the
-// kernels bank-conflict free on the 64 x 4-byte LDS banks: 16 lanes reading
-// the same logical chunk of 16 different rows, and a transposing read (4
-// consecutive rows x 2 adjacent chunks per 16-lane group).  fp32 tiles (512-byte
-// rows, only read one float per lane) stay unpermuted.
+// chunk' = chunk ^ swz(r), a function of r mod 16.  The permutation makes the
+// read patterns of the kernels bank-conflict free on the 64 x 4-byte LDS banks:
+//  - 16-byte operand reads, served 16 lanes at a time: 16 rows (in order, or
+//    in the rperm order) at one logical chunk, so swz must be one-to-one on
+//    16 rows;
+//  - transposing 8-byte reads, served 32 lanes at a time: 4 consecutive rows
+//    (aligned to 4) x 4 consecutive chunks (aligned to 4), so those 4 rows must
+//    move the chunk group (swz >> 2) to 4 different places.
+// For 256-byte rows swz swaps the two 2-bit halves of r mod 16; 128-byte rows
+// share a bank cycle in pairs, so r's lowest bit is left out.  fp32 tiles
+// (512-byte rows, only read one float per lane) stay unpermuted.
 template <int ROWB>
 struct SwzTile {
   static constexpr int CPR = ROWB / 16;  // 16-byte chunks per row
   __device__ __forceinline__ static int swz(int r) {
-    if constexpr (CPR == 16) return ((r & 7) << 1) | ((r >> 3) & 1);
-    else if constexpr (CPR == 8) return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
+    if constexpr (CPR == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else if constexpr (CPR == 8) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
     else return 0;
   }
   // Byte offset of logical byte `colb` of row r.
