@@ -91,6 +91,15 @@ WORKLOADS: Dict[str, Workload] = {
                  _isqrt(128), _isqrt(128), Recipe("iid", amp1=4.0), "mean", seed=104),
         Workload("causal_128k_h8_d128_d64", 1, 8, 131072, 131072, 128, 64, "bf16", True,
                  _isqrt(128), _isqrt(64), Recipe("iid"), "mean", seed=105),
+        # Long contexts on one GPU (the pages claim up to 512K).
+        Workload("causal_256k_h4_d128", 1, 4, 262144, 262144, 128, 128, "bf16", True,
+                 _isqrt(128), _isqrt(128), Recipe("corr", noise=0.5), "mean", seed=106),
+        Workload("causal_512k_h2_d128", 1, 2, 524288, 524288, 128, 128, "bf16", True,
+                 _isqrt(128), _isqrt(128), Recipe("corr", noise=0.5), "mean", seed=107),
+        # A 1024-query chunk at the end of a 256K causal sequence (bottom-right
+        # aligned): few query tiles, many keys -- the split-K regime.
+        Workload("chunk_1k_of_256k_h8_d128", 1, 8, 1024, 262144, 128, 128, "bf16", True,
+                 _isqrt(128), _isqrt(128), Recipe("corr", noise=0.3), "mean", seed=108),
     ]
 }
 

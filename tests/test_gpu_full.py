@@ -150,3 +150,55 @@ def test_causal_128k_indexer_student(gpu_lib, store):
                                           w.scale1, w.scale2, True)
     torch.cuda.synchronize()
     check_sampled_backward(w, dq, dk, "student")
+
+
+@pytest.mark.parametrize("name", ["causal_256k_h4_d128", "causal_512k_h2_d128"])
+def test_long_context_forward_and_both_backward(gpu_lib, store, name):
+    """256K and 512K contexts on one GPU: sampled rows, trailing key columns
+    and sum_j dK_j = 0, for the forward and both backward settings."""
+    w, t = inputs(store, name)
+    say(f"[full] {name} forward")
+    kl, l1, l2 = gpu_lib.skl_forward(t["q1"], t["k1"], t["q2"], t["k2"], w.scale1, w.scale2, True)
+    torch.cuda.synchronize()
+    check_sampled_forward(w, kl, l1, l2)
+    for setting in ("student", "teacher"):
+        say(f"[full] {name} {setting} backward")
+        if setting == "student":
+            dq, dk = gpu_lib.skl_backward_student(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, t["g"],
+                                                  w.scale1, w.scale2, True)
+        else:
+            dq, dk = gpu_lib.skl_backward_teacher(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, kl, t["g"],
+                                                  w.scale1, w.scale2, True)
+        torch.cuda.synchronize()
+        check_sampled_backward(w, dq, dk, setting)
+        del dq, dk
+
+
+def test_query_chunk_of_long_sequence(gpu_lib, store):
+    """1024 queries at the end of a 256K causal sequence (bottom-right
+    alignment): few query tiles, so the recommended split count is > 1; the
+    split-K forward agrees with the plain one and both match the oracle."""
+    w, t = inputs(store, "chunk_1k_of_256k_h8_d128")
+    say("[full] 1K-query chunk of 256K: forward")
+    kl, l1, l2 = gpu_lib.skl_forward(t["q1"], t["k1"], t["q2"], t["k2"], w.scale1, w.scale2, True)
+    torch.cuda.synchronize()
+    check_sampled_forward(w, kl, l1, l2)
+    splits = gpu_lib.skl_recommended_splits(t["q1"], t["k1"], t["q2"], t["k2"], True)
+    assert splits > 1
+    say(f"[full] 1K-query chunk of 256K: split-K {splits}")
+    ws, n = gpu_lib.skl_forward_splitk(t["q1"], t["k1"], t["q2"], t["k2"], w.scale1, w.scale2, True, splits)
+    skl_kl, s1, s2 = gpu_lib.skl_reduce(ws, n, w.B, w.H, w.NQ)
+    torch.cuda.synchronize()
+    for a, b_ in ((skl_kl, kl), (s1, l1), (s2, l2)):
+        assert torch.allclose(a, b_, rtol=2e-5, atol=2e-5)
+    for setting in ("student", "teacher"):
+        say(f"[full] 1K-query chunk of 256K: {setting} backward")
+        if setting == "student":
+            dq, dk = gpu_lib.skl_backward_student(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, t["g"],
+                                                  w.scale1, w.scale2, True)
+        else:
+            dq, dk = gpu_lib.skl_backward_teacher(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, kl, t["g"],
+                                                  w.scale1, w.scale2, True)
+        torch.cuda.synchronize()
+        check_sampled_backward(w, dq, dk, setting)
+        del dq, dk
