@@ -1,6 +1,9 @@
 // C-ABI entry points of libstreamkl: argument validation, workspace sizing and
 // kernel dispatch.  Every check runs on the host before anything is enqueued.
 
+#include <algorithm>
+#include <atomic>
+#include <cstdint>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -250,11 +253,57 @@ skl_status skl_reduce(const skl_shape* s, int num_splits, const void* ws, size_t
   return from_hip(skl::launch_reduce(p, stream), "skl_reduce launch");
 }
 
+}  // extern "C"
+
+namespace {
+
+// Compute units of the current device (cached per device id).
+int current_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Key ranges of the split backward's dQ kernel.  Its workgroups own 128
+// queries each; when those alone cannot fill the device (two resident
+// workgroups per CU) the keys are cut into ranges of at least 8 tiles.
+int64_t dq_splits_for(const skl_shape* s) {
+  const int cus = current_cus();
+  if (cus <= 0) return 1;
+  const int64_t target = 2 * (int64_t)cus;
+  const int64_t tiles = s->B * s->H * cdiv(s->NQ, 128);
+  if (tiles <= 0 || tiles >= target) return 1;
+  int64_t splits = cdiv(target, tiles);
+  splits = std::min<int64_t>(splits, cdiv(s->NK, 8 * skl::kDqBK));
+  splits = std::min<int64_t>(splits, 64);
+  return std::max<int64_t>(splits, 1);
+}
+
+int64_t dq_split_len(const skl_shape* s, int64_t splits) {
+  return cdiv(cdiv(s->NK, splits), skl::kDqBK) * skl::kDqBK;
+}
+
+}  // namespace
+
+extern "C" {
+
 size_t skl_backward_workspace_size(const skl_shape* s, int teacher, int algo) {
-  if (!s || s->B < 0 || s->H < 0 || s->NQ < 0 || algo != SKL_BWD_FUSED_ATOMIC) return 0;
+  if (!s || s->B <= 0 || s->H <= 0 || s->NQ <= 0 || s->NK <= 0) return 0;
   const int d = teacher ? s->d1 : s->d2;
   if (d <= 0) return 0;
-  return (size_t)s->B * (size_t)s->H * (size_t)s->NQ * (size_t)d * sizeof(float);
+  const size_t plane = (size_t)s->B * (size_t)s->H * (size_t)s->NQ * (size_t)d * sizeof(float);
+  if (algo == SKL_BWD_FUSED_ATOMIC) return plane;
+  if (algo != SKL_BWD_SPLIT) return 0;
+  const int64_t splits = dq_splits_for(s);
+  return splits > 1 ? (size_t)splits * plane : 0;
 }
 
 static skl_status backward_common(const skl_shape* s, const void* q1, const void* k1, const void* q2,
@@ -308,11 +357,43 @@ static skl_status backward_common(const skl_shape* s, const void* q1, const void
   p.sdq = teacher ? p.sq1 : p.sq2;
   p.ws = static_cast<float*>(ws);
 
+  skl::ConvertParams c{};
+  c.dq = dq;
+  c.sdq = teacher ? p.sq1 : p.sq2;
+  c.NQ = s->NQ;
+  c.H = (int32_t)s->H;
+  c.dg = dg;
+  c.rows = BH * s->NQ;
+  c.scale = scale_g;
+  c.splits = 1;
+  c.split_stride = c.rows * dg;
+
   if (!fused) {
+    // With the workspace skl_backward_workspace_size() asks for, the dQ kernel
+    // splits its keys into ranges whose fp32 partials convert_kernel sums;
+    // without it (or when the query tiles fill the device) dQ is written
+    // directly.
+    const int64_t splits = dq_splits_for(s);
+    const size_t need = skl_backward_workspace_size(s, teacher ? 1 : 0, algo);
+    const bool split_dq = splits > 1 && ws != nullptr && ws_bytes >= need;
+    if (split_dq) {
+      if (reinterpret_cast<uintptr_t>(ws) % 16 != 0) return fail(SKL_ERR_UNSUPPORTED, "ws must be 16-byte aligned");
+      p.dq_splits = (int32_t)splits;
+      p.dq_split_len = (int32_t)dq_split_len(s, splits);
+      p.dq_part = static_cast<float*>(ws);
+    } else {
+      p.dq_splits = 1;
+    }
     hipError_t e = mark(0, stream);
     if (e == hipSuccess)
       e = skl::launch_backward_split(p, s->dtype, s->d1, s->d2, causal != 0, teacher, BH, stream, mark1);
     if (e == hipSuccess) e = mark(2, stream);
+    if (e == hipSuccess && split_dq) {
+      c.ws = p.dq_part;
+      c.splits = (int32_t)splits;
+      e = skl::launch_convert(c, s->dtype, stream);
+      if (e == hipSuccess) e = mark(3, stream);
+    }
     return from_hip(e, "backward launch");
   }
 
@@ -323,15 +404,7 @@ static skl_status backward_common(const skl_shape* s, const void* q1, const void
   });
   if (e != hipSuccess) return from_hip(e, "backward launch");
 
-  skl::ConvertParams c{};
   c.ws = static_cast<const float*>(ws);
-  c.dq = dq;
-  c.sdq = teacher ? p.sq1 : p.sq2;
-  c.NQ = s->NQ;
-  c.H = (int32_t)s->H;
-  c.dg = dg;
-  c.rows = BH * s->NQ;
-  c.scale = scale_g;
   return from_hip(skl::launch_convert(c, s->dtype, stream), "dq convert launch");
 }
 

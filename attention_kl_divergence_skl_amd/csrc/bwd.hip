@@ -272,7 +272,14 @@ __global__ __launch_bounds__(256) void convert_kernel(const ConvertParams p) {
     const int d0 = (int)(i % per_row) * V;
     const int64_t bh = row / p.NQ, q = row % p.NQ;
     const int64_t b = bh / p.H, h = bh % p.H;
-    const float4 v = reinterpret_cast<const float4*>(p.ws)[i];
+    float4 v = reinterpret_cast<const float4*>(p.ws)[i];
+    for (int sp = 1; sp < p.splits; ++sp) {
+      const float4 u = reinterpret_cast<const float4*>(p.ws + sp * p.split_stride)[i];
+      v.x += u.x;
+      v.y += u.y;
+      v.z += u.z;
+      v.w += u.w;
+    }
     T* dst = reinterpret_cast<T*>(p.dq) + b * p.sdq.b + h * p.sdq.h + q * p.sdq.n + d0;
     dst[0] = from_f32<T>(v.x * p.scale);
     dst[1] = from_f32<T>(v.y * p.scale);

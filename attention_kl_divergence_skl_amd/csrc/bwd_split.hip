@@ -301,7 +301,12 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kerne
   const int half = lane >> 5, col = lane & 31;
 
   const int num_qtiles = (int)((p.NQ + BQ - 1) / BQ);
-  const int64_t t = xcd_remap(blockIdx.x, gridDim.x);
+  int64_t t = xcd_remap(blockIdx.x, gridDim.x);
+  int split = 0;  // key range of this workgroup when the keys are split (few query tiles)
+  if (p.dq_splits > 1) {
+    split = (int)(t % p.dq_splits);
+    t /= p.dq_splits;
+  }
   const int64_t bh = t / num_qtiles;
   int qt = (int)(t % num_qtiles);
   if (CAUSAL) qt = num_qtiles - 1 - qt;  // longest rows first
@@ -338,9 +343,13 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kerne
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) dq[cb] = f32x16{};
 
-  int64_t kend = p.NK;
+  int64_t kbeg = 0, kend = p.NK;
   if (CAUSAL) kend = min(kend, (int64_t)(qt + 1) * BQ + off);
-  const int64_t nsteps = (kend + BK - 1) / BK;
+  if (p.dq_splits > 1) {
+    kbeg = (int64_t)split * p.dq_split_len;
+    kend = min(kend, kbeg + (int64_t)p.dq_split_len);
+  }
+  const int64_t nsteps = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
   const int64_t wave_kmax = CAUSAL ? qw0 + 31 + off : p.NK - 1;
 
   auto fetch = [&](int st, int64_t j0) {
@@ -348,7 +357,7 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kerne
     tile_load_async<BK, RB2>(sK2[st], k2p, p.sk2.n * ESZ, j0, p.NK, wave, lane);
   };
 
-  if (nsteps > 0) fetch(0, 0);
+  if (nsteps > 0) fetch(0, kbeg);
   wait_vm();
   __syncthreads();
   const float c1 = p.c1, c2 = p.c2;
@@ -359,7 +368,7 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kerne
   auto step = [&](auto masked, int64_t it) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked)::value;
     const int st = (int)(it & 1);
-    const int64_t j0 = it * BK;
+    const int64_t j0 = kbeg + it * BK;
     if (it + 1 < nsteps) fetch(st ^ 1, j0 + BK);
 
     if (!MASKED || wave_uniform(j0 <= wave_kmax)) {
@@ -426,20 +435,33 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kerne
   };
   // Steps [tail, nsteps) reach the causal diagonal of some wave (keys past
   // qt 128 + off - 63) or the ragged key edge; a ragged query tile masks all.
+  // Both conditions hold from some step on; first_ge(x) is the first step
+  // whose first key is >= x.
+  auto first_ge = [&](int64_t x) -> int64_t { return x <= kbeg ? 0 : (x - kbeg + BK - 1) / BK; };
   int64_t tail = 0;
   if ((int64_t)qt * BQ + BQ <= p.NQ) {
-    tail = nsteps;
-    if (p.NK % BK != 0) tail = nsteps - 1;
-    // step it is masked iff it BK >= qt BQ + off - BK + 2 =: y
-    const int64_t y = (int64_t)qt * BQ + off - BK + 2;
-    if (CAUSAL) tail = min(tail, y > 0 ? (y + BK - 1) / BK : (int64_t)0);
-    tail = max(tail, (int64_t)0);
+    tail = min(nsteps, first_ge(p.NK - BK + 1));
+    if (CAUSAL) tail = min(tail, first_ge((int64_t)qt * BQ + off - BK + 2));
   }
   int64_t it = 0;
   for (; it < tail; ++it) step(std::false_type{}, it);
   for (; it < nsteps; ++it) step(std::true_type{}, it);
 
   // dQ of this wave's rows: accumulator register r holds query qw0 + acc_row(r, half).
+  if (p.dq_splits > 1) {
+    // Unscaled fp32 partial of this key range (zeros for an empty range);
+    // convert_kernel sums the ranges and applies the scale.
+    const int64_t BH = gridDim.x / ((int64_t)num_qtiles * p.dq_splits);
+    float* const dst = p.dq_part + ((int64_t)split * BH + bh) * p.NQ * DG;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t q = qw0 + acc_row(r, half);
+        if (q < p.NQ) dst[q * DG + 32 * cb + col] = dq[cb][r];
+      }
+    return;
+  }
   char* const dqp = (char*)p.dq + (b * p.sdq.b + h * p.sdq.h) * ESZ;
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb)
@@ -460,7 +482,7 @@ hipError_t run_split(const BwdParams& p, int64_t BH, hipStream_t s, void (*betwe
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (between) between(s);
-  const int64_t gq = BH * ((p.NQ + 127) / 128);
+  const int64_t gq = BH * ((p.NQ + 127) / 128) * (p.dq_splits > 1 ? p.dq_splits : 1);
   hipLaunchKernelGGL((bwd_dq_kernel<T, D1, D2, C, TCH>), dim3((unsigned)gq), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }

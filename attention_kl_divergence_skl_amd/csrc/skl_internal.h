@@ -68,10 +68,15 @@ struct BwdParams {
   void* dq;             // gradient of the optimised side's queries (split kernels)
   Strides sdq;
   float* ws;            // fp32 dQ accumulator [B*H][NQ][dg] (fused kernel)
+  int32_t dq_splits;    // split kernels: key ranges of the dQ kernel (1: write dq directly)
+  int32_t dq_split_len; // keys per range (multiple of kDqBK)
+  float* dq_part;       // dq_splits > 1: unscaled fp32 partials [dq_splits][B*H][NQ][dg]
 };
 
 struct ConvertParams {
-  const float* ws;
+  const float* ws;      // [splits][rows][dg] fp32, summed over splits
+  int32_t splits;
+  int64_t split_stride; // elements between split planes (rows * dg)
   void* dq;
   Strides sdq;
   int64_t NQ;

@@ -65,8 +65,12 @@ typedef enum skl_dtype { SKL_BF16 = 0, SKL_F32 = 1 } skl_dtype;
 /*
  * Backward algorithms.
  *  SKL_BWD_SPLIT (default): one kernel owns keys and writes dK, one owns
- *    queries and writes dQ; both recompute the two logit tiles.  No
- *    workspace, no atomics, bitwise deterministic.
+ *    queries and writes dQ; both recompute the two logit tiles.  No atomics,
+ *    bitwise deterministic.  The workspace is optional: when the query tiles
+ *    alone cannot fill the device (few heads x queries, many keys -- the
+ *    regime of split-K) and the caller passes skl_backward_workspace_size()
+ *    bytes, the dQ kernel splits its keys into ranges whose fp32 partials a
+ *    reduce kernel sums; otherwise dQ is written directly.
  *  SKL_BWD_FUSED_ATOMIC: one kernel visits each (query tile, key tile) pair
  *    once, keeps dK on chip and adds dQ into an fp32 workspace with atomics
  *    (article section "GPU kernel optimisations", fused backward); needs
@@ -126,9 +130,15 @@ skl_status skl_reduce(const skl_shape* shape, int num_splits, const void* ws, si
                       float* kl, float* lse1, float* lse2, hipStream_t stream);
 
 /*
- * Workspace bytes a backward call with algorithm `algo` needs: 0 for
- * SKL_BWD_SPLIT; for SKL_BWD_FUSED_ATOMIC the fp32 dQ accumulator,
- * 4 * B * H * N_Q * d with d = d2 (teacher == 0) or d1 (teacher != 0).
+ * Workspace bytes a backward call with algorithm `algo` uses, with
+ * d = d2 (teacher == 0) or d1 (teacher != 0):
+ *  SKL_BWD_FUSED_ATOMIC: the fp32 dQ accumulator, 4 * B * H * N_Q * d
+ *    (required);
+ *  SKL_BWD_SPLIT: 0 when B * H * ceil(N_Q / 128) query tiles fill the
+ *    current device (two per compute unit), else S * 4 * B * H * N_Q * d for
+ *    the S key ranges of the dQ kernel (S <= 64, each range >= 512 keys);
+ *    optional, see skl_bwd_algo.  The value depends on the current device's
+ *    compute-unit count.
  */
 size_t skl_backward_workspace_size(const skl_shape* shape, int teacher, int algo);
 
@@ -140,7 +150,9 @@ size_t skl_backward_workspace_size(const skl_shape* shape, int teacher, int algo
  * tile-by-tile gradients"), with the kernels of `algo` (skl_bwd_algo).
  * dq2 and dk2 have the element type of the inputs and the same strides as
  * q2 and k2 respectively.  ws: skl_backward_workspace_size(shape, 0, algo)
- * bytes, 16-byte aligned (may be NULL when that is 0); the call clears it.
+ * bytes, 16-byte aligned, owned by the caller and overwritten by the call.
+ * It may be NULL when that size is 0; for SKL_BWD_SPLIT it may be NULL (or
+ * smaller) in any case, and the dQ kernel then runs over all keys unsplit.
  */
 skl_status skl_backward_student(const skl_shape* shape,
                                 const void* q1, const void* k1, const void* q2, const void* k2,

@@ -9,7 +9,7 @@ import torch
 
 import oracle
 from attention_kl_divergence_skl_amd import synth
-from tests.gpu_util import (check_grad, check_rows, gpu_forward, grad_to_np, oracle_backward,
+from tests.gpu_util import (TOL, check_grad, check_rows, gpu_forward, grad_to_np, oracle_backward,
                             oracle_forward, say, to_device)
 
 pytestmark = pytest.mark.gpu
@@ -58,19 +58,23 @@ def test_forward_matches_oracle(gpu_lib, w):
     check_rows(w.name, w, got, oracle_forward(w, x))
 
 
-@pytest.mark.parametrize("algo", ["split", "fused_atomic"])
+@pytest.mark.parametrize("algo", ["split", "split_no_ws", "fused_atomic"])
 @pytest.mark.parametrize("setting", ["student", "teacher"])
 @pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
 def test_backward_matches_oracle(gpu_lib, w, setting, algo):
+    """split: dQ over key ranges whenever the query tiles are few (all of
+    these shapes); split_no_ws: the same kernels with dQ over all keys."""
     say(f"[backward {setting} {algo}] {w.name}")
     x, t = to_device(w)
     _, (kl, l1, l2) = gpu_forward(gpu_lib, w, t)
+    ws = torch.empty(0, dtype=torch.float32, device="cuda") if algo == "split_no_ws" else None
+    a = "split" if algo == "split_no_ws" else algo
     if setting == "student":
         dq, dk = gpu_lib.skl_backward_student(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, t["g"],
-                                              w.scale1, w.scale2, w.causal, algo=algo)
+                                              w.scale1, w.scale2, w.causal, algo=a, ws=ws)
     else:
         dq, dk = gpu_lib.skl_backward_teacher(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, kl, t["g"],
-                                              w.scale1, w.scale2, w.causal, algo=algo)
+                                              w.scale1, w.scale2, w.causal, algo=a, ws=ws)
     torch.cuda.synchronize()
     rq, rk = oracle_backward(w, x, setting)
     check_grad(f"{w.name} dQ ({setting})", w, grad_to_np(dq), rq)
@@ -195,6 +199,46 @@ def test_backward_run_to_run_variation(gpu_lib, algo):
             assert torch.equal(dq, outs[0][0])
         rel = float((dq - outs[0][0]).norm() / outs[0][0].norm())
         assert rel <= 1e-2 * 1e-2
+
+
+KEY_SPLIT_CASES = [
+    W("ks_bf16_causal_chunk", 1, 2, 100, 3000, 128, 128, "bf16", True, synth.Recipe("corr", noise=0.3)),
+    W("ks_bf16_noncausal", 1, 1, 200, 2100, 128, 64, "bf16", False),
+    W("ks_f32_causal", 1, 1, 130, 1500, 64, 64, "f32", True),
+    W("ks_bf16_causal_square", 1, 1, 700, 700, 64, 128, "bf16", True),
+]
+
+
+@pytest.mark.parametrize("setting", ["student", "teacher"])
+@pytest.mark.parametrize("w", KEY_SPLIT_CASES, ids=lambda w: w.name)
+def test_backward_dq_key_ranges(gpu_lib, w, setting):
+    """Few query tiles: the split backward's dQ kernel cuts the keys into
+    ranges whose partials are summed.  Against the oracle, against the
+    unsplit dQ (zero-size workspace), and bitwise repeatable."""
+    say(f"[backward dQ key ranges {setting}] {w.name}")
+    x, t = to_device(w)
+    _, (kl, l1, l2) = gpu_forward(gpu_lib, w, t)
+    assert gpu_lib.skl_backward_workspace_size(t["q1"], t["k1"], t["q2"], t["k2"], setting == "teacher") > 0
+
+    def run(ws=None):
+        if setting == "student":
+            return gpu_lib.skl_backward_student(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, t["g"],
+                                                w.scale1, w.scale2, w.causal, ws=ws)
+        return gpu_lib.skl_backward_teacher(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, kl, t["g"],
+                                            w.scale1, w.scale2, w.causal, ws=ws)
+
+    dq, dk = run()
+    dq_again, _ = run()
+    dq_whole, dk_whole = run(ws=torch.empty(0, dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+    rq, rk = oracle_backward(w, x, setting)
+    check_grad(f"{w.name} dQ ({setting}, key ranges)", w, grad_to_np(dq), rq)
+    check_grad(f"{w.name} dK ({setting})", w, grad_to_np(dk), rk)
+    check_grad(f"{w.name} dQ ({setting}, unsplit)", w, grad_to_np(dq_whole), rq)
+    assert torch.equal(dq, dq_again), "key-range partials are summed in a fixed order"
+    assert torch.equal(dk, dk_whole), "dK does not depend on the dQ key ranges"
+    rel = float((dq.float() - dq_whole.float()).norm() / dq_whole.float().norm())
+    assert rel <= TOL[w.dtype]["grad"]
 
 
 def test_split_and_fused_backward_agree(gpu_lib):
