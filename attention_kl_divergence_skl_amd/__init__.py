@@ -308,3 +308,58 @@ def skl_recommended_splits(q1, k1, q2, k2, causal: bool = False, num_cus: Option
         num_cus = torch.cuda.get_device_properties(q1.device).multi_processor_count
     s = make_shape(q1, k1, q2, k2)
     return int(load().skl_recommended_splits(ctypes.byref(s), int(bool(causal)), int(num_cus)))
+
+
+# ---------------------------------------------------------------------------
+# Autograd wrapper: per-row KL(P1 || P2) as a differentiable torch op.  P1
+# does not depend on (Q2, K2) and P2 does not depend on (Q1, K1), so the
+# student call ("optimise P2") gives exactly dKL/d(Q2, K2) and the teacher
+# call ("optimise P1") exactly dKL/d(Q1, K1); backward launches only the
+# settings whose inputs require a gradient (a frozen teacher costs one).
+# ---------------------------------------------------------------------------
+
+def _autograd_function():
+    import torch
+
+    class AttentionKL(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q1, k1, q2, k2, scale1, scale2, causal, algo):
+            kl, lse1, lse2 = skl_forward(q1, k1, q2, k2, scale1, scale2, causal)
+            ctx.save_for_backward(q1, k1, q2, k2, kl, lse1, lse2)
+            ctx.args = (scale1, scale2, causal, algo)
+            ctx.mark_non_differentiable(lse1, lse2)
+            return kl, lse1, lse2
+
+        @staticmethod
+        def backward(ctx, g, _g_lse1, _g_lse2):
+            q1, k1, q2, k2, kl, lse1, lse2 = ctx.saved_tensors
+            scale1, scale2, causal, algo = ctx.args
+            g = g.float().contiguous()
+            dq1 = dk1 = dq2 = dk2 = None
+            if ctx.needs_input_grad[2] or ctx.needs_input_grad[3]:
+                dq2, dk2 = skl_backward_student(q1, k1, q2, k2, lse1, lse2, g, scale1, scale2, causal, algo=algo)
+            if ctx.needs_input_grad[0] or ctx.needs_input_grad[1]:
+                dq1, dk1 = skl_backward_teacher(q1, k1, q2, k2, lse1, lse2, kl, g, scale1, scale2, causal,
+                                                algo=algo)
+            return dq1, dk1, dq2, dk2, None, None, None, None
+
+    return AttentionKL
+
+
+_ATTENTION_KL = None
+
+
+def attention_kl(q1, k1, q2, k2, scale1=None, scale2=None, causal: bool = False, algo="split"):
+    """Differentiable per-row KL(P1 || P2), P_k = softmax(scale_k Q_k K_k^T).
+
+    Returns (kl, lse1, lse2); kl [B, H, N_Q] fp32 carries gradients to every
+    input that requires one (the LSEs are auxiliary and not differentiable).
+    Scales default to 1/sqrt(d_k)."""
+    global _ATTENTION_KL
+    if _ATTENTION_KL is None:
+        _ATTENTION_KL = _autograd_function()
+    s1, s2 = _scales(q1, q2, scale1, scale2)
+    return _ATTENTION_KL.apply(q1, k1, q2, k2, s1, s2, bool(causal), algo)
+
+
+__all__ += ["attention_kl"]
