@@ -19,7 +19,8 @@ from typing import Optional, Tuple
 
 __all__ = [
     "load", "SklError", "skl_forward", "skl_forward_splitk", "skl_reduce",
-    "skl_backward_student", "skl_backward_teacher", "skl_recommended_splits",
+    "skl_backward_student", "skl_backward_teacher", "skl_backward_joint", "skl_recommended_splits",
+    "skl_backward_joint_workspace_size",
     "skl_forward_splitk_workspace_size", "skl_backward_workspace_size",
     "skl_version", "skl_set_kernel_events", "LIB_PATH",
 ]
@@ -64,6 +65,8 @@ _SIGS = {
     "skl_backward_workspace_size": (_SZ, [_SP, _I, _I]),
     "skl_backward_student": (_I, [_SP, _P, _P, _P, _P, _F, _F, _I, _P, _P, _P, _P, _P, _I, _P, _SZ, _P]),
     "skl_backward_teacher": (_I, [_SP, _P, _P, _P, _P, _F, _F, _I, _P, _P, _P, _P, _P, _P, _I, _P, _SZ, _P]),
+    "skl_backward_joint_workspace_size": (_SZ, [_SP]),
+    "skl_backward_joint": (_I, [_SP, _P, _P, _P, _P, _F, _F, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "skl_recommended_splits": (_I, [_SP, _I, _I]),
     "skl_status_string": (ctypes.c_char_p, [_I]),
     "skl_last_error": (ctypes.c_char_p, []),
@@ -301,6 +304,33 @@ def skl_backward_teacher(q1, k1, q2, k2, lse1, lse2, kl, dkl, scale1=None, scale
     return dq1, dk1
 
 
+def skl_backward_joint_workspace_size(q1, k1, q2, k2) -> int:
+    s = make_shape(q1, k1, q2, k2)
+    return int(load().skl_backward_joint_workspace_size(ctypes.byref(s)))
+
+
+def skl_backward_joint(q1, k1, q2, k2, lse1, lse2, kl, dkl, scale1=None, scale2=None,
+                       causal: bool = False, ws=None) -> Tuple:
+    """(dq1, dk1, dq2, dk2): both settings in one pass; dtype and strides of
+    q1, k1, q2, k2."""
+    import torch
+
+    _check_device(q1, k1, q2, k2, lse1, lse2, kl, dkl)
+    s = make_shape(q1, k1, q2, k2)
+    s1, s2 = _scales(q1, q2, scale1, scale2)
+    for t, n in ((lse1, "lse1"), (lse2, "lse2"), (kl, "kl"), (dkl, "dkl")):
+        _rowvec(t, s.B, s.H, s.NQ, n)
+    dq1, dk1, dq2, dk2 = _grad_like(q1), _grad_like(k1), _grad_like(q2), _grad_like(k2)
+    need = int(load().skl_backward_joint_workspace_size(ctypes.byref(s)))
+    if need and ws is None:
+        ws = torch.empty(need // 4, dtype=torch.float32, device=q1.device)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load().skl_backward_joint(ctypes.byref(s), _ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), s1, s2,
+                                     int(causal), _ptr(lse1), _ptr(lse2), _ptr(kl), _ptr(dkl), _ptr(dq1),
+                                     _ptr(dk1), _ptr(dq2), _ptr(dk2), _ptr(ws), nbytes, _stream(q1)))
+    return dq1, dk1, dq2, dk2
+
+
 def skl_recommended_splits(q1, k1, q2, k2, causal: bool = False, num_cus: Optional[int] = None) -> int:
     if num_cus is None:
         import torch
@@ -315,7 +345,8 @@ def skl_recommended_splits(q1, k1, q2, k2, causal: bool = False, num_cus: Option
 # does not depend on (Q2, K2) and P2 does not depend on (Q1, K1), so the
 # student call ("optimise P2") gives exactly dKL/d(Q2, K2) and the teacher
 # call ("optimise P1") exactly dKL/d(Q1, K1); backward launches only the
-# settings whose inputs require a gradient (a frozen teacher costs one).
+# settings whose inputs require a gradient (a frozen teacher costs one; both
+# at once use the joint kernels).
 # ---------------------------------------------------------------------------
 
 def _autograd_function():
@@ -336,9 +367,14 @@ def _autograd_function():
             scale1, scale2, causal, algo = ctx.args
             g = g.float().contiguous()
             dq1 = dk1 = dq2 = dk2 = None
-            if ctx.needs_input_grad[2] or ctx.needs_input_grad[3]:
+            need_s = ctx.needs_input_grad[2] or ctx.needs_input_grad[3]
+            need_t = ctx.needs_input_grad[0] or ctx.needs_input_grad[1]
+            if need_s and need_t and algo == "split":
+                dq1, dk1, dq2, dk2 = skl_backward_joint(q1, k1, q2, k2, lse1, lse2, kl, g, scale1, scale2, causal)
+                return dq1, dk1, dq2, dk2, None, None, None, None
+            if need_s:
                 dq2, dk2 = skl_backward_student(q1, k1, q2, k2, lse1, lse2, g, scale1, scale2, causal, algo=algo)
-            if ctx.needs_input_grad[0] or ctx.needs_input_grad[1]:
+            if need_t:
                 dq1, dk1 = skl_backward_teacher(q1, k1, q2, k2, lse1, lse2, kl, g, scale1, scale2, causal,
                                                 algo=algo)
             return dq1, dk1, dq2, dk2, None, None, None, None

@@ -424,6 +424,74 @@ skl_status skl_backward_teacher(const skl_shape* s, const void* q1, const void* 
                          ws_bytes, true, stream);
 }
 
+size_t skl_backward_joint_workspace_size(const skl_shape* s) {
+  return skl_backward_workspace_size(s, 0, SKL_BWD_SPLIT) + skl_backward_workspace_size(s, 1, SKL_BWD_SPLIT);
+}
+
+skl_status skl_backward_joint(const skl_shape* s, const void* q1, const void* k1, const void* q2, const void* k2,
+                              float scale1, float scale2, int causal, const float* lse1, const float* lse2,
+                              const float* kl, const float* dkl, void* dq1, void* dk1, void* dq2, void* dk2,
+                              void* ws, size_t ws_bytes, hipStream_t stream) {
+  SKL_TRY(check_inputs(s, q1, k1, q2, k2, scale1, scale2, causal));
+  if (empty(s)) return ok();
+  SKL_TRY(check_ptr(lse1, "lse1", false));
+  SKL_TRY(check_ptr(lse2, "lse2", false));
+  SKL_TRY(check_ptr(kl, "kl", false));
+  SKL_TRY(check_ptr(dkl, "dkl", false));
+  SKL_TRY(check_ptr(dq1, "dq1"));
+  SKL_TRY(check_ptr(dk1, "dk1"));
+  SKL_TRY(check_ptr(dq2, "dq2"));
+  SKL_TRY(check_ptr(dk2, "dk2"));
+
+  const size_t need_s = skl_backward_workspace_size(s, 0, SKL_BWD_SPLIT);
+  const size_t need_t = skl_backward_workspace_size(s, 1, SKL_BWD_SPLIT);
+  if (need_s + need_t > 0 && ws != nullptr && ws_bytes >= need_s + need_t) {
+    // Few query tiles and the workspace to split the keys of dQ: the two
+    // settings one after the other, each with its dQ over key ranges.
+    skl_status st = backward_common(s, q1, k1, q2, k2, scale1, scale2, causal, lse1, lse2, nullptr, dkl, dq2, dk2,
+                                    SKL_BWD_SPLIT, ws, need_s, false, stream);
+    if (st != SKL_OK) return st;
+    return backward_common(s, q1, k1, q2, k2, scale1, scale2, causal, lse1, lse2, kl, dkl, dq1, dk1, SKL_BWD_SPLIT,
+                           static_cast<char*>(ws) + need_s, need_t, true, stream);
+  }
+
+  const int64_t BH = s->B * s->H;
+  skl::BwdParams p{};
+  p.q1 = q1;
+  p.k1 = k1;
+  p.q2 = q2;
+  p.k2 = k2;
+  p.sq1 = strides(s->sq1);
+  p.sk1 = strides(s->sk1);
+  p.sq2 = strides(s->sq2);
+  p.sk2 = strides(s->sk2);
+  p.NQ = s->NQ;
+  p.NK = s->NK;
+  p.H = (int32_t)s->H;
+  p.num_ktiles = (int32_t)cdiv(s->NK, skl::kBwdBK);
+  p.c1 = (float)(scale1 * 1.4426950408889634);
+  p.c2 = (float)(scale2 * 1.4426950408889634);
+  p.lse1 = lse1;
+  p.lse2 = lse2;
+  p.kl = kl;
+  p.dkl = dkl;
+  p.dk = dk1;
+  p.sdk = p.sk1;
+  p.dq = dq1;
+  p.sdq = p.sq1;
+  p.scale_g = scale1;
+  p.dk_s = dk2;
+  p.sdk_s = p.sk2;
+  p.dq_s = dq2;
+  p.sdq_s = p.sq2;
+  p.scale_s = scale2;
+  p.dq_splits = 1;
+  hipError_t e = mark(0, stream);
+  if (e == hipSuccess) e = skl::launch_backward_joint(p, s->dtype, s->d1, s->d2, causal != 0, BH, stream, mark1);
+  if (e == hipSuccess) e = mark(2, stream);
+  return from_hip(e, "joint backward launch");
+}
+
 int skl_recommended_splits(const skl_shape* s, int causal, int num_cus) {
   if (!s || s->B <= 0 || s->H <= 0 || s->NQ <= 0 || s->NK <= 0 || num_cus <= 0) return 1;
   // Two resident forward workgroups per CU; aim for at least two waves of them.

@@ -1,0 +1,483 @@
+// Joint backward of the attention-KL primitive for gfx950: the gradients of
+// both settings -- (Q1, K1) for "optimise P1" and (Q2, K2) for "optimise P2"
+// -- from one recompute of the two logit tiles and one pair of exponentials
+// per (query, key) pair.
+//
+// Both settings rebuild P_k = 2^(t_k - LSE_k log2 e) tile by tile from the
+// saved LSEs (agidaily.cc StreamKL article, section "Backward:
+// recompute-based tile-by-tile gradients") and share every step up to dS:
+//   dS2 = g (P2 - P1)                    (student, P1 fixed)
+//   dS1 = g P1 (ln2 (u1 - u2) - KL)      (teacher, P2 fixed; u_k = t_k - L_k)
+// so one kernel pass per side of the contraction produces all four
+// gradients: the joint dK kernel owns keys (dK1 += dS1ᵀ Q1, dK2 += dS2ᵀ Q2),
+// the joint dQ kernel owns queries (dQ1 += dS1 K1, dQ2 += dS2 K2).  Against
+// the two settings run one after the other this saves one logit recompute
+// and one exponential per pair in each kernel.
+//
+// The two sets of gradient accumulators (128 fp32 registers per lane at
+// d = 128) do not fit two waves per SIMD, so these kernels run one wave per
+// SIMD with the accumulators in the accumulation registers.  Per matrix
+// instruction they need about one exponential and four other vector ops,
+// a mix a single wave can hide behind its MFMAs when the instruction stream
+// interleaves the two; as compiled (matrix phase, then vector phase, per
+// block) they run at about the speed of the two settings one after the
+// other.  The tile layout, operand orders and masking follow bwd_split.hip.
+
+#include <type_traits>
+
+#include "skl_device.h"
+#include "skl_internal.h"
+
+namespace skl {
+
+namespace {
+
+// Both dS values of one accumulator element from the raw logits and the row
+// constants L_k = LSE_k log2 e, g, gl = g ln2 and gk = g KL.
+__device__ __forceinline__ void dS_both(float s1, float s2, float c1, float c2, float L1, float L2, float g,
+                                        float gl, float gk, float& ds1, float& ds2) {
+  const float u1 = fmaf(s1, c1, -L1);
+  const float u2 = fmaf(s2, c2, -L2);
+  const float p1 = exp2_hw(u1), p2 = exp2_hw(u2);
+  ds2 = g * (p2 - p1);
+  ds1 = p1 * fmaf(gl, u1 - u2, -gk);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Joint dK kernel: 4 waves own 128 keys (32 each) of one (b, h) and walk the
+// query tiles of 64 rows that see them, 32 rows at a time.  K fragments of
+// both sides stay in registers; Q1/Q2 tiles come straight into a
+// double-buffered swizzled LDS ring with the row constants (L1, L2, g, g KL)
+// beside them.
+// ---------------------------------------------------------------------------
+template <typename T, int D1, int D2, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void bwd_joint_dk_kernel(const BwdParams p) {
+  using M = Mfma<T>;
+  using frag = typename M::frag;
+  constexpr int KC = M::KC, EPL = M::EPL;
+  constexpr int NC1 = D1 / KC, NC2 = D2 / KC;
+  constexpr int NB1 = D1 / 32, NB2 = D2 / 32;  // 32-wide column blocks of dK1 / dK2
+  constexpr int ESZ = sizeof(T);
+  constexpr int BQ = kDkBQ;
+  constexpr int RB1 = D1 * ESZ, RB2 = D2 * ESZ;  // bytes per query row
+  using T1 = SwzTile<RB1>;
+  using T2 = SwzTile<RB2>;
+
+  __shared__ __attribute__((aligned(1024))) char sQ1[2][BQ * RB1];
+  __shared__ __attribute__((aligned(1024))) char sQ2[2][BQ * RB2];
+  __shared__ __attribute__((aligned(16))) float sVec[2][4][BQ];  // L1, L2 (base 2), g, g KL
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5, col = lane & 31;
+
+  const int64_t t = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t bh = t / p.num_ktiles;
+  const int kt = (int)(t % p.num_ktiles);
+  const int64_t b = bh / p.H, h = bh % p.H;
+  const int64_t off = p.NK - p.NQ;
+  const int64_t kt0 = (int64_t)kt * kBwdBK;
+  const int64_t kw0 = kt0 + 32 * wave;
+  const int64_t key = kw0 + col;
+  const bool kvalid = key < p.NK;
+
+  const char* const q1p = (const char*)p.q1 + (b * p.sq1.b + h * p.sq1.h) * ESZ;
+  const char* const q2p = (const char*)p.q2 + (b * p.sq2.b + h * p.sq2.h) * ESZ;
+  const char* const k1p = (const char*)p.k1 + (b * p.sk1.b + h * p.sk1.h) * ESZ;
+  const char* const k2p = (const char*)p.k2 + (b * p.sk2.b + h * p.sk2.h) * ESZ;
+
+  frag kf1[NC1], kf2[NC2];
+#pragma unroll
+  for (int c = 0; c < NC1; ++c)
+    kf1[c] = kvalid ? M::load(k1p + (key * p.sk1.n + c * KC + half * EPL) * ESZ) : M::zero();
+#pragma unroll
+  for (int c = 0; c < NC2; ++c)
+    kf2[c] = kvalid ? M::load(k2p + (key * p.sk2.n + c * KC + half * EPL) * ESZ) : M::zero();
+
+  f32x16 dk1[NB1], dk2[NB2];
+#pragma unroll
+  for (int cb = 0; cb < NB1; ++cb) dk1[cb] = f32x16{};
+#pragma unroll
+  for (int cb = 0; cb < NB2; ++cb) dk2[cb] = f32x16{};
+
+  int64_t qbeg = 0;
+  if (CAUSAL) qbeg = max((int64_t)0, kt0 - off) / BQ * BQ;
+  const int64_t nsteps = (p.NQ - qbeg + BQ - 1) / BQ;
+
+  float pv = 0.f;
+  auto fetch = [&](int st, int64_t q0) {
+    tile_load_async<BQ, RB1>(sQ1[st], q1p, p.sq1.n * ESZ, q0, p.NQ, wave, lane);
+    tile_load_async<BQ, RB2>(sQ2[st], q2p, p.sq2.n * ESZ, q0, p.NQ, wave, lane);
+    pv = 0.f;
+    if (tid < 4 * BQ) {
+      const int which = tid / BQ, row = tid % BQ;
+      const int64_t q = q0 + row;
+      if (q < p.NQ) {
+        const int64_t o = bh * p.NQ + q;
+        if (which == 0) pv = p.lse1[o] * kLog2e;
+        else if (which == 1) pv = p.lse2[o] * kLog2e;
+        else if (which == 2) pv = p.dkl[o];
+        else pv = p.dkl[o] * p.kl[o];
+      }
+    }
+  };
+  auto stash = [&](int st) {
+    if (tid < 4 * BQ) sVec[st][tid / BQ][tid % BQ] = pv;
+  };
+
+  if (nsteps > 0) {
+    fetch(0, qbeg);
+    stash(0);
+  }
+  wait_vm();
+  __syncthreads();
+  const float c1 = p.c1, c2 = p.c2;
+  const int prow = rperm(col);
+  const SwzAddr<RB1> ad1(prow, half, lane);
+  const SwzAddr<RB2> ad2(prow, half, lane);
+
+  auto step = [&](auto masked, int64_t it) __attribute__((always_inline)) {
+    const int st = (int)(it & 1);
+    constexpr bool MASKED = decltype(masked)::value;
+    const int64_t q0 = qbeg + it * BQ;
+    if (it + 1 < nsteps) fetch(st ^ 1, q0 + BQ);
+
+    const SwzAddr<RB1> x1 = ad1.shifted(st * BQ * RB1);
+    const SwzAddr<RB2> x2 = ad2.shifted(st * BQ * RB2);
+#pragma unroll
+    for (int qb = 0; qb < BQ / 32; ++qb) {
+      const int64_t qb0 = q0 + 32 * qb;
+      if (MASKED && (kw0 >= p.NK || qb0 >= p.NQ || (CAUSAL && kw0 > qb0 + 31 + off))) continue;  // fully masked
+      f32x16 s1 = f32x16{}, s2 = f32x16{};
+      if constexpr (EPL == 1) {
+        const int qrow = 32 * qb + prow;
+#pragma unroll
+        for (int c = 0; c < NC1; ++c)
+          s1 = M::run(M::load(&sQ1[st][T1::off(qrow, (c * KC + half * EPL) * ESZ)]), kf1[c], s1);
+#pragma unroll
+        for (int c = 0; c < NC2; ++c)
+          s2 = M::run(M::load(&sQ2[st][T2::off(qrow, (c * KC + half * EPL) * ESZ)]), kf2[c], s2);
+      } else {
+#pragma unroll
+        for (int c = 0; c < NC1; ++c) s1 = M::run(x1.frag(sQ1[0], 32 * qb * RB1, c), kf1[c], s1);
+#pragma unroll
+        for (int c = 0; c < NC2; ++c) s2 = M::run(x2.frag(sQ2[0], 32 * qb * RB2, c), kf2[c], s2);
+      }
+
+      // Registers 8 run .. 8 run + 7 hold rows 32 qb + 16 run + 8 half + 0..7
+      // (the rperm order): they form K chunk `run` (bf16) or chunks
+      // 8 run .. 8 run + 7 (fp32) of both dK products.
+      const bool need_mask = MASKED && ((qb0 + 32 > p.NQ) || (kw0 + 32 > p.NK) || (CAUSAL && kw0 + 31 > qb0 + off));
+      const int qlim = clamp_i32(p.NQ - qb0), cmin = clamp_i32(key - qb0 - off);
+#pragma unroll
+      for (int run = 0; run < 2; ++run) {
+        float cst[4][8];
+#pragma unroll
+        for (int which = 0; which < 4; ++which) {
+          const float4* v = reinterpret_cast<const float4*>(&sVec[st][which][32 * qb + 16 * run + 8 * half]);
+          const float4 y0 = v[0], y1 = v[1];
+          cst[which][0] = y0.x; cst[which][1] = y0.y; cst[which][2] = y0.z; cst[which][3] = y0.w;
+          cst[which][4] = y1.x; cst[which][5] = y1.y; cst[which][6] = y1.z; cst[which][7] = y1.w;
+        }
+        float ds1[8], ds2[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int r = 8 * run + i;
+          dS_both(s1[r], s2[r], c1, c2, cst[0][i], cst[1][i], cst[2][i], cst[2][i] * kLn2, cst[3][i], ds1[i],
+                  ds2[i]);
+        }
+        if (need_mask) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int ro = rloc(8 * run + i, half);
+            const bool vis = kvalid && ro < qlim && (!CAUSAL || ro >= cmin);
+            ds1[i] = vis ? ds1[i] : 0.f;
+            ds2[i] = vis ? ds2[i] : 0.f;
+          }
+        }
+        if constexpr (EPL == 1) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int c = 8 * run + i;
+            const int qr = 32 * qb + rloc(c, half);
+#pragma unroll
+            for (int cb = 0; cb < NB1; ++cb)
+              dk1[cb] = M::run(ds1[i], *reinterpret_cast<const float*>(&sQ1[st][T1::off(qr, (32 * cb + col) * ESZ)]),
+                               dk1[cb]);
+#pragma unroll
+            for (int cb = 0; cb < NB2; ++cb)
+              dk2[cb] = M::run(ds2[i], *reinterpret_cast<const float*>(&sQ2[st][T2::off(qr, (32 * cb + col) * ESZ)]),
+                               dk2[cb]);
+          }
+        } else {
+          frag a1, a2;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) {
+            a1[e] = from_f32<T>(ds1[e]);
+            a2[e] = from_f32<T>(ds2[e]);
+          }
+#pragma unroll
+          for (int cb = 0; cb < NB1; ++cb) dk1[cb] = M::run(a1, x1.trfrag(sQ1[0], (32 * qb + run * KC) * RB1, cb), dk1[cb]);
+#pragma unroll
+          for (int cb = 0; cb < NB2; ++cb) dk2[cb] = M::run(a2, x2.trfrag(sQ2[0], (32 * qb + run * KC) * RB2, cb), dk2[cb]);
+        }
+      }
+    }
+    if (it + 1 < nsteps) stash(st ^ 1);
+    wait_vm();
+    __syncthreads();
+  };
+  // Steps [0, head) reach the causal diagonal, [tail, nsteps) the ragged
+  // query edge; a ragged key tile masks every step.
+  int64_t head = 0, tail = nsteps;
+  if (kt0 + kBwdBK > p.NK) {
+    head = nsteps;
+  } else {
+    const int64_t x = kt0 + kBwdBK - 1 - off - qbeg;
+    if (CAUSAL && x > 0) head = min(nsteps, (x + BQ - 1) / BQ);
+    if (p.NQ % BQ != 0) tail = max(head, nsteps - 1);
+  }
+  int64_t it = 0;
+  for (; it < head; ++it) step(std::true_type{}, it);
+  for (; it < tail; ++it) step(std::false_type{}, it);
+  for (; it < nsteps; ++it) step(std::true_type{}, it);
+
+  char* const dk1p = (char*)p.dk + (b * p.sdk.b + h * p.sdk.h) * ESZ;
+  char* const dk2p = (char*)p.dk_s + (b * p.sdk_s.b + h * p.sdk_s.h) * ESZ;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int64_t kk = kw0 + acc_row(r, half);
+    if (kk < p.NK) {
+#pragma unroll
+      for (int cb = 0; cb < NB1; ++cb)
+        *reinterpret_cast<T*>(dk1p + (kk * p.sdk.n + 32 * cb + col) * ESZ) = from_f32<T>(dk1[cb][r] * p.scale_g);
+#pragma unroll
+      for (int cb = 0; cb < NB2; ++cb)
+        *reinterpret_cast<T*>(dk2p + (kk * p.sdk_s.n + 32 * cb + col) * ESZ) = from_f32<T>(dk2[cb][r] * p.scale_s);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Joint dQ kernel: 4 waves own 128 queries (32 each) of one (b, h) and stream
+// the 64-key tiles they see.  Per 32-key block each wave forms Sᵀ = K Qᵀ
+// (query = accumulator column, Q in registers), both dS with per-lane row
+// constants, dQ1 += dS1 K1 and dQ2 += dS2 K2.
+// ---------------------------------------------------------------------------
+template <typename T, int D1, int D2, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void bwd_joint_dq_kernel(const BwdParams p) {
+  using M = Mfma<T>;
+  using frag = typename M::frag;
+  constexpr int KC = M::KC, EPL = M::EPL;
+  constexpr int NC1 = D1 / KC, NC2 = D2 / KC;
+  constexpr int NB1 = D1 / 32, NB2 = D2 / 32;
+  constexpr int ESZ = sizeof(T);
+  constexpr int BQ = 128, BK = kDqBK;
+  constexpr int RB1 = D1 * ESZ, RB2 = D2 * ESZ;  // bytes per key row
+  using T1 = SwzTile<RB1>;
+  using T2 = SwzTile<RB2>;
+
+  __shared__ __attribute__((aligned(1024))) char sK1[2][BK * RB1];
+  __shared__ __attribute__((aligned(1024))) char sK2[2][BK * RB2];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5, col = lane & 31;
+
+  const int num_qtiles = (int)((p.NQ + BQ - 1) / BQ);
+  const int64_t t = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t bh = t / num_qtiles;
+  int qt = (int)(t % num_qtiles);
+  if (CAUSAL) qt = num_qtiles - 1 - qt;  // longest rows first
+  const int64_t b = bh / p.H, h = bh % p.H;
+  const int64_t off = p.NK - p.NQ;
+  const int64_t qw0 = (int64_t)qt * BQ + 32 * wave;
+  const int64_t qi = qw0 + col;
+  const bool qvalid = qi < p.NQ;
+
+  const char* const q1p = (const char*)p.q1 + (b * p.sq1.b + h * p.sq1.h) * ESZ;
+  const char* const q2p = (const char*)p.q2 + (b * p.sq2.b + h * p.sq2.h) * ESZ;
+  const char* const k1p = (const char*)p.k1 + (b * p.sk1.b + h * p.sk1.h) * ESZ;
+  const char* const k2p = (const char*)p.k2 + (b * p.sk2.b + h * p.sk2.h) * ESZ;
+
+  frag qf1[NC1], qf2[NC2];
+#pragma unroll
+  for (int c = 0; c < NC1; ++c)
+    qf1[c] = qvalid ? M::load(q1p + (qi * p.sq1.n + c * KC + half * EPL) * ESZ) : M::zero();
+#pragma unroll
+  for (int c = 0; c < NC2; ++c)
+    qf2[c] = qvalid ? M::load(q2p + (qi * p.sq2.n + c * KC + half * EPL) * ESZ) : M::zero();
+
+  float L1 = 0.f, L2 = 0.f, g = 0.f, gk = 0.f;
+  if (qvalid) {
+    const int64_t o = bh * p.NQ + qi;
+    L1 = p.lse1[o] * kLog2e;
+    L2 = p.lse2[o] * kLog2e;
+    g = p.dkl[o];
+    gk = p.dkl[o] * p.kl[o];
+  }
+  const float gl = g * kLn2;
+
+  f32x16 dq1[NB1], dq2[NB2];
+#pragma unroll
+  for (int cb = 0; cb < NB1; ++cb) dq1[cb] = f32x16{};
+#pragma unroll
+  for (int cb = 0; cb < NB2; ++cb) dq2[cb] = f32x16{};
+
+  int64_t kend = p.NK;
+  if (CAUSAL) kend = min(kend, (int64_t)(qt + 1) * BQ + off);
+  const int64_t nsteps = kend > 0 ? (kend + BK - 1) / BK : 0;
+  const int64_t wave_kmax = CAUSAL ? qw0 + 31 + off : p.NK - 1;
+
+  auto fetch = [&](int st, int64_t j0) {
+    tile_load_async<BK, RB1>(sK1[st], k1p, p.sk1.n * ESZ, j0, p.NK, wave, lane);
+    tile_load_async<BK, RB2>(sK2[st], k2p, p.sk2.n * ESZ, j0, p.NK, wave, lane);
+  };
+
+  if (nsteps > 0) fetch(0, 0);
+  wait_vm();
+  __syncthreads();
+  const float c1 = p.c1, c2 = p.c2;
+  const int prow = rperm(col);
+
+  auto step = [&](auto masked, int64_t it) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked)::value;
+    const int st = (int)(it & 1);
+    const int64_t j0 = it * BK;
+    if (it + 1 < nsteps) fetch(st ^ 1, j0 + BK);
+
+    if (!MASKED || wave_uniform(j0 <= wave_kmax)) {
+      const bool need_mask =
+          MASKED && wave_uniform((j0 + BK > p.NK) || (CAUSAL && j0 + BK - 1 > qw0 + off) || (qw0 + 32 > p.NQ));
+#pragma unroll
+      for (int kb = 0; kb < BK / 32; ++kb) {
+        f32x16 s1 = f32x16{}, s2 = f32x16{};
+        const int klim = clamp_i32(p.NK - (j0 + kb * 32)), cmax = clamp_i32(qi + off - (j0 + kb * 32));
+        const int krow = kb * 32 + prow;
+#pragma unroll
+        for (int c = 0; c < NC1; ++c)
+          s1 = M::run(M::load(&sK1[st][T1::off(krow, (c * KC + half * EPL) * ESZ)]), qf1[c], s1);
+#pragma unroll
+        for (int c = 0; c < NC2; ++c)
+          s2 = M::run(M::load(&sK2[st][T2::off(krow, (c * KC + half * EPL) * ESZ)]), qf2[c], s2);
+        // Registers 8 run .. 8 run + 7 hold keys kb 32 + 16 run + 8 half + 0..7.
+#pragma unroll
+        for (int run = 0; run < 2; ++run) {
+          float ds1[8], ds2[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int r = 8 * run + i;
+            dS_both(s1[r], s2[r], c1, c2, L1, L2, g, gl, gk, ds1[i], ds2[i]);
+          }
+          if (need_mask) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const int ro = rloc(8 * run + i, half);
+              const bool vis = qvalid && ro < klim && (!CAUSAL || ro <= cmax);
+              ds1[i] = vis ? ds1[i] : 0.f;
+              ds2[i] = vis ? ds2[i] : 0.f;
+            }
+          }
+          if constexpr (EPL == 1) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const int kr = kb * 32 + rloc(8 * run + i, half);
+#pragma unroll
+              for (int cb = 0; cb < NB1; ++cb)
+                dq1[cb] = M::run(ds1[i], *reinterpret_cast<const float*>(&sK1[st][T1::off(kr, (32 * cb + col) * ESZ)]),
+                                 dq1[cb]);
+#pragma unroll
+              for (int cb = 0; cb < NB2; ++cb)
+                dq2[cb] = M::run(ds2[i], *reinterpret_cast<const float*>(&sK2[st][T2::off(kr, (32 * cb + col) * ESZ)]),
+                                 dq2[cb]);
+            }
+          } else {
+            frag a1, a2;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+              a1[e] = from_f32<T>(ds1[e]);
+              a2[e] = from_f32<T>(ds2[e]);
+            }
+#pragma unroll
+            for (int cb = 0; cb < NB1; ++cb)
+              dq1[cb] = M::run(a1, lds_tr_frag_swz<RB1>(&sK1[st][0], kb * 32 + run * KC, 32 * cb, lane), dq1[cb]);
+#pragma unroll
+            for (int cb = 0; cb < NB2; ++cb)
+              dq2[cb] = M::run(a2, lds_tr_frag_swz<RB2>(&sK2[st][0], kb * 32 + run * KC, 32 * cb, lane), dq2[cb]);
+          }
+        }
+      }
+    }
+    wait_vm();
+    __syncthreads();
+  };
+  // Steps [tail, nsteps) reach the causal diagonal of some wave or the ragged
+  // key edge; a ragged query tile masks all (see bwd_split.hip).
+  auto first_ge = [&](int64_t x) -> int64_t { return x <= 0 ? 0 : (x + BK - 1) / BK; };
+  int64_t tail = 0;
+  if ((int64_t)qt * BQ + BQ <= p.NQ) {
+    tail = min(nsteps, first_ge(p.NK - BK + 1));
+    if (CAUSAL) tail = min(tail, first_ge((int64_t)qt * BQ + off - BK + 2));
+  }
+  int64_t it = 0;
+  for (; it < tail; ++it) step(std::false_type{}, it);
+  for (; it < nsteps; ++it) step(std::true_type{}, it);
+
+  char* const dq1p = (char*)p.dq + (b * p.sdq.b + h * p.sdq.h) * ESZ;
+  char* const dq2p = (char*)p.dq_s + (b * p.sdq_s.b + h * p.sdq_s.h) * ESZ;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int64_t q = qw0 + acc_row(r, half);
+    if (q < p.NQ) {
+#pragma unroll
+      for (int cb = 0; cb < NB1; ++cb)
+        *reinterpret_cast<T*>(dq1p + (q * p.sdq.n + 32 * cb + col) * ESZ) = from_f32<T>(dq1[cb][r] * p.scale_g);
+#pragma unroll
+      for (int cb = 0; cb < NB2; ++cb)
+        *reinterpret_cast<T*>(dq2p + (q * p.sdq_s.n + 32 * cb + col) * ESZ) = from_f32<T>(dq2[cb][r] * p.scale_s);
+    }
+  }
+}
+
+namespace {
+
+template <typename T, int D1, int D2, bool C>
+hipError_t run_joint(const BwdParams& p, int64_t BH, hipStream_t s, void (*between)(hipStream_t)) {
+  const int64_t gk = BH * p.num_ktiles;
+  hipLaunchKernelGGL((bwd_joint_dk_kernel<T, D1, D2, C>), dim3((unsigned)gk), dim3(kThreads), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (between) between(s);
+  const int64_t gq = BH * ((p.NQ + 127) / 128);
+  hipLaunchKernelGGL((bwd_joint_dq_kernel<T, D1, D2, C>), dim3((unsigned)gq), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+template <typename T, int D1, int D2>
+hipError_t joint_dims(const BwdParams& p, bool causal, int64_t BH, hipStream_t s, void (*bw)(hipStream_t)) {
+  return causal ? run_joint<T, D1, D2, true>(p, BH, s, bw) : run_joint<T, D1, D2, false>(p, BH, s, bw);
+}
+
+template <typename T>
+hipError_t joint_type(const BwdParams& p, int d1, int d2, bool causal, int64_t BH, hipStream_t s,
+                      void (*bw)(hipStream_t)) {
+  if (d1 == 128 && d2 == 128) return joint_dims<T, 128, 128>(p, causal, BH, s, bw);
+  if (d1 == 128 && d2 == 64) return joint_dims<T, 128, 64>(p, causal, BH, s, bw);
+  if (d1 == 64 && d2 == 128) return joint_dims<T, 64, 128>(p, causal, BH, s, bw);
+  if (d1 == 64 && d2 == 64) return joint_dims<T, 64, 64>(p, causal, BH, s, bw);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_backward_joint(const BwdParams& p, int dtype, int d1, int d2, bool causal, int64_t BH,
+                                 hipStream_t s, void (*between)(hipStream_t)) {
+  if (dtype == 0) return joint_type<bf16>(p, d1, d2, causal, BH, s, between);
+  return joint_type<float>(p, d1, d2, causal, BH, s, between);
+}
+
+}  // namespace skl

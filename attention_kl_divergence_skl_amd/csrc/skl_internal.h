@@ -68,6 +68,13 @@ struct BwdParams {
   void* dq;             // gradient of the optimised side's queries (split kernels)
   Strides sdq;
   float* ws;            // fp32 dQ accumulator [B*H][NQ][dg] (fused kernel)
+  // Joint kernels (both settings at once): dk/dq/scale_g above are the
+  // teacher's (Q1, K1) gradients, these the student's (Q2, K2).
+  void* dk_s;
+  Strides sdk_s;
+  void* dq_s;
+  Strides sdq_s;
+  float scale_s;
   int32_t dq_splits;    // split kernels: key ranges of the dQ kernel (1: write dq directly)
   int32_t dq_split_len; // keys per range (multiple of kDqBK)
   float* dq_part;       // dq_splits > 1: unscaled fp32 partials [dq_splits][B*H][NQ][dg]
@@ -98,6 +105,9 @@ hipError_t launch_backward_fused(const BwdParams& p, int dtype, int d1, int d2, 
 // `between` runs after the first launch (profiling events).
 hipError_t launch_backward_split(const BwdParams& p, int dtype, int d1, int d2, bool causal, bool teacher,
                                  int64_t BH, hipStream_t s, void (*between)(hipStream_t));
+// Both settings in one pass (joint dK kernel, then joint dQ kernel).
+hipError_t launch_backward_joint(const BwdParams& p, int dtype, int d1, int d2, bool causal, int64_t BH,
+                                 hipStream_t s, void (*between)(hipStream_t));
 hipError_t launch_convert(const ConvertParams& p, int dtype, hipStream_t s);
 
 }  // namespace skl

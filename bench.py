@@ -4,7 +4,9 @@
 One step = one pass of the whole hot path over one batch of synthetic input
 already resident in HBM: skl_forward (one-pass forward), then
 skl_backward_student (optimise P2) and skl_backward_teacher (optimise P1),
-each with its workspace clear and dQ convert.  W untimed warm-up steps, then
+each a dK kernel and a dQ kernel (--bwd-algo joint: one skl_backward_joint
+call for both settings; fused_atomic: the fused kernel with its workspace
+clear and dQ convert).  W untimed warm-up steps, then
 exactly K timed steps between two device synchronisations.
 
 Prints ONE JSON line.  `value` is the step's algorithmic TFLOP/s
@@ -35,6 +37,8 @@ KERNEL_SOURCES = {
     "bwd_dk_kernel": ["bwd_split.hip", "skl_device.h", "skl_internal.h"],
     "bwd_dq_kernel": ["bwd_split.hip", "skl_device.h", "skl_internal.h"],
     "bwd_fused_kernel": ["bwd.hip", "skl_device.h", "skl_internal.h"],
+    "bwd_joint_dk_kernel": ["bwd_joint.hip", "skl_device.h", "skl_internal.h"],
+    "bwd_joint_dq_kernel": ["bwd_joint.hip", "skl_device.h", "skl_internal.h"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.txt")
 
@@ -129,6 +133,9 @@ def kernel_flops(w, wk, phase: str, algo: str):
     P = wk.pairs
     if phase == "fwd":
         return {"fwd_kernel": wk.fwd_flops}
+    if phase == "joint":  # both logits once + the four gradient GEMMs, split over two kernels
+        per = 2 * P * 2 * (w.d1 + w.d2)
+        return {"bwd_joint_dk_kernel": per, "bwd_joint_dq_kernel": per}
     dg = w.d2 if phase == "student" else w.d1
     if algo == "split":
         per = 2 * P * (w.d1 + w.d2 + dg)  # both logits again + one gradient GEMM
@@ -143,8 +150,10 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--phases", default="fwd,student,teacher",
-                    help="comma list of fwd, student, teacher (profiling aid; the default is the full step)")
-    ap.add_argument("--bwd-algo", default="split", choices=["split", "fused_atomic"])
+                    help="comma list of fwd, student, teacher, joint (profiling aid; the default is the "
+                         "full step; --bwd-algo joint turns student,teacher into joint)")
+    ap.add_argument("--bwd-algo", default="split", choices=["split", "fused_atomic", "joint"],
+                    help="joint: both settings in one skl_backward_joint call")
     ap.add_argument("--cpu-sub", type=int, default=16384, help="side of the causal block the oracle times")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MiB",
@@ -174,10 +183,12 @@ def main(argv=None) -> int:
 
     w = synth.WORKLOADS[args.workload]
     phases = [p for p in args.phases.split(",") if p]
-    for p in phases:
-        if p not in ("fwd", "student", "teacher"):
-            raise SystemExit(f"unknown phase {p}")
     algo = args.bwd_algo
+    if algo == "joint":
+        phases = [p for p in phases if p not in ("student", "teacher")] + ["joint"]
+    for p in phases:
+        if p not in ("fwd", "student", "teacher", "joint"):
+            raise SystemExit(f"unknown phase {p}")
     log(f"workload {w.name}: generating inputs")
     t0 = time.perf_counter()
     t = synth.device_inputs(w, "cuda")
@@ -189,7 +200,10 @@ def main(argv=None) -> int:
 
     # Workspaces (fused algorithm only) are allocated once, outside the timed region.
     def ws_for(teacher):
-        n = skl.skl_backward_workspace_size(q1, k1, q2, k2, teacher, algo)
+        if algo == "joint":
+            n = skl.skl_backward_joint_workspace_size(q1, k1, q2, k2) if teacher else 0
+        else:
+            n = skl.skl_backward_workspace_size(q1, k1, q2, k2, teacher, algo)
         return torch.empty(n // 4, dtype=torch.float32, device="cuda") if n else None
 
     ws_s, ws_t = ws_for(False), ws_for(True)
@@ -206,7 +220,7 @@ def main(argv=None) -> int:
     def step(record: bool):
         out = {}
         kl = l1 = l2 = None
-        for p in ("fwd", "student", "teacher"):
+        for p in ("fwd", "student", "teacher", "joint"):
             if not (p in phases or (p == "fwd" and phases != ["fwd"])):
                 continue
             rec = record and p in phases
@@ -217,6 +231,9 @@ def main(argv=None) -> int:
                 ce[0].record()
             if p == "fwd":
                 kl, l1, l2 = skl.skl_forward(q1, k1, q2, k2, w.scale1, w.scale2, w.causal)
+            elif p == "joint":
+                out["j"] = skl.skl_backward_joint(q1, k1, q2, k2, l1, l2, kl, g, w.scale1, w.scale2, w.causal,
+                                                  ws=ws_t)
             elif p == "student":
                 out["s"] = skl.skl_backward_student(q1, k1, q2, k2, l1, l2, g, w.scale1, w.scale2, w.causal,
                                                     algo=algo, ws=ws_s)
@@ -256,7 +273,8 @@ def main(argv=None) -> int:
     log(f"{args.steps} timed steps in {elapsed:.3f} s")
 
     peak_tf = workmodel.PEAK_BF16_DENSE_TFLOPS if w.dtype == "bf16" else workmodel.PEAK_FP32_MFMA_TFLOPS
-    alg = {"fwd": wk.fwd_flops, "student": wk.student_flops, "teacher": wk.teacher_flops}
+    alg = {"fwd": wk.fwd_flops, "student": wk.student_flops, "teacher": wk.teacher_flops,
+           "joint": wk.student_flops + wk.teacher_flops}
     report, kernels = {}, []
     for p in phases:
         call_ms = float(np.mean([a.elapsed_time(b) for a, b in pev[p]]))

@@ -179,6 +179,32 @@ skl_status skl_backward_teacher(const skl_shape* shape,
                                 size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Both settings in one pass: (dq1, dk1) as skl_backward_teacher and
+ * (dq2, dk2) as skl_backward_student would write them, from one recompute of
+ * the two logit tiles and one pair of exponentials per (query, key) pair --
+ * the two settings share every step up to dS (article section "Backward:
+ * recompute-based tile-by-tile gradients").  With the student's and the
+ * teacher's calls together this is the gradient of sum_i dkl_i KL_i with
+ * respect to all four inputs.  Kernels: a joint dK kernel and a joint dQ
+ * kernel (no atomics, bitwise deterministic).  ws is optional:
+ * skl_backward_joint_workspace_size(shape) is nonzero only when the query
+ * tiles alone cannot fill the device, and given that many bytes (16-byte
+ * aligned) the call runs the two SKL_BWD_SPLIT settings one after the other
+ * instead, each with its dQ over key ranges (the student's workspace first,
+ * then the teacher's); with ws NULL it always runs the joint kernels.  Outputs
+ * have the dtype of the inputs and the strides of q1, k1, q2, k2.  Event
+ * slots (skl_set_kernel_events): 0 before, 1 after the joint dK kernel, 2
+ * after the joint dQ kernel.
+ */
+size_t skl_backward_joint_workspace_size(const skl_shape* shape);
+skl_status skl_backward_joint(const skl_shape* shape,
+                              const void* q1, const void* k1, const void* q2, const void* k2,
+                              float scale1, float scale2, int causal,
+                              const float* lse1, const float* lse2, const float* kl, const float* dkl,
+                              void* dq1, void* dk1, void* dq2, void* dk2,
+                              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Split count that fills a GPU with `num_cus` compute units for this shape
  * (1 when the query tiles alone fill it).  Pure host arithmetic.
  */

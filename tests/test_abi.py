@@ -152,3 +152,13 @@ def test_recommended_splits(lib):
     assert 2 <= k <= 64
     tiny = _shape(B=1, H=1, NQ=128, NK=128)
     assert lib.skl_recommended_splits(ctypes.byref(tiny), 0, 256) == 1
+
+
+def test_joint_backward_validation(lib):
+    s = _shape()
+    st = lib.skl_backward_joint(ctypes.byref(s), *P, 0.1, 0.1, 0, A, A, None, A, A, A, A, A, None, 0, None)
+    assert st == INVALID   # kl is required
+    st = lib.skl_backward_joint(ctypes.byref(s), *P, 0.1, 0.1, 0, A, A, A, A, A, A, None, A, None, 0, None)
+    assert st == INVALID   # every gradient output is required
+    st = lib.skl_backward_joint(ctypes.byref(s), *P, 0.1, 0.1, 2, A, A, A, A, A, A, A + 4, A, None, 0, None)
+    assert st in (INVALID, UNSUPPORTED)

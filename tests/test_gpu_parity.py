@@ -264,3 +264,49 @@ def test_errors_raise_before_launch(gpu_lib):
     with pytest.raises(gpu_lib.SklError):
         gpu_lib.skl_forward(t["q1"][..., :96].contiguous(), t["k1"][..., :96].contiguous(),
                             t["q2"], t["k2"], 0.1, 0.1, False)
+
+
+@pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
+def test_joint_backward_matches_oracle(gpu_lib, w):
+    """Both settings in one pass (joint kernels, no workspace): all four
+    gradients against the oracle, and against the two separate calls."""
+    say(f"[joint backward] {w.name}")
+    x, t = to_device(w)
+    _, (kl, l1, l2) = gpu_forward(gpu_lib, w, t)
+    none = torch.empty(0, dtype=torch.float32, device="cuda")
+    dq1, dk1, dq2, dk2 = gpu_lib.skl_backward_joint(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, kl, t["g"],
+                                                    w.scale1, w.scale2, w.causal, ws=none)
+    again = gpu_lib.skl_backward_joint(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, kl, t["g"],
+                                       w.scale1, w.scale2, w.causal, ws=none)
+    sq2, sk2 = gpu_lib.skl_backward_student(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, t["g"],
+                                            w.scale1, w.scale2, w.causal, ws=none)
+    sq1, sk1 = gpu_lib.skl_backward_teacher(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, kl, t["g"],
+                                            w.scale1, w.scale2, w.causal, ws=none)
+    torch.cuda.synchronize()
+    for a, b_ in zip((dq1, dk1, dq2, dk2), again):
+        assert torch.equal(a, b_), "joint backward is bitwise deterministic"
+    for setting, dq, dk, sq, sk in (("teacher", dq1, dk1, sq1, sk1), ("student", dq2, dk2, sq2, sk2)):
+        rq, rk = oracle_backward(w, x, setting)
+        check_grad(f"{w.name} joint dQ ({setting})", w, grad_to_np(dq), rq)
+        check_grad(f"{w.name} joint dK ({setting})", w, grad_to_np(dk), rk)
+        for a, b_ in ((dq, sq), (dk, sk)):
+            den = float(b_.float().norm())
+            if den > 0:
+                assert float((a.float() - b_.float()).norm()) <= 1e-5 * den
+
+
+@pytest.mark.parametrize("w", KEY_SPLIT_CASES[:2], ids=lambda w: w.name)
+def test_joint_backward_with_key_range_workspace(gpu_lib, w):
+    """Few query tiles and the workspace: the joint call runs both settings
+    with key-split dQ."""
+    say(f"[joint backward, key ranges] {w.name}")
+    x, t = to_device(w)
+    _, (kl, l1, l2) = gpu_forward(gpu_lib, w, t)
+    assert gpu_lib.skl_backward_joint_workspace_size(t["q1"], t["k1"], t["q2"], t["k2"]) > 0
+    dq1, dk1, dq2, dk2 = gpu_lib.skl_backward_joint(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, kl, t["g"],
+                                                    w.scale1, w.scale2, w.causal)
+    torch.cuda.synchronize()
+    for setting, dq, dk in (("teacher", dq1, dk1), ("student", dq2, dk2)):
+        rq, rk = oracle_backward(w, x, setting)
+        check_grad(f"{w.name} joint dQ ({setting})", w, grad_to_np(dq), rq)
+        check_grad(f"{w.name} joint dK ({setting})", w, grad_to_np(dk), rk)
