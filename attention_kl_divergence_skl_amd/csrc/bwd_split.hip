@@ -16,6 +16,12 @@
 // plain stores, and the result is bitwise deterministic.  (The fused kernel
 // remains available as SKL_BWD_FUSED_ATOMIC.)
 //
+// When the query tiles alone are too few to fill the GPU (few heads and
+// queries, many keys) the dQ kernel also cuts its keys into tile-aligned
+// ranges: each (query tile, key range) workgroup writes an unscaled fp32
+// partial and convert_kernel sums them in a fixed order, so the result stays
+// deterministic.
+//
 // Both kernels form logits with the rows of the streamed operand loaded in
 // the rperm order, so an accumulator register block is directly the A operand
 // of the gradient MFMA; the other operand of that MFMA comes from a row-major
