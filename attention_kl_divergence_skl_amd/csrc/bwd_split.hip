@@ -149,9 +149,7 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dk_kerne
   __syncthreads();
   const float c1 = p.c1, c2 = p.c2;
   const int prow = rperm(col);
-  // LDS address bases (bf16 tiles; unused by the fp32 instantiations).
-  const SwzAddr<RB1> ad1(prow, half, lane);
-  const SwzAddr<RB2> ad2(prow, half, lane);
+  // LDS address base of the gradient operand (bf16 tiles; unused in fp32).
   const SwzAddr<RBG> adg(prow, half, lane);
 
   // One query step.  The stage (which LDS buffer) is a template constant so
@@ -167,8 +165,6 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dk_kerne
 
     const char* qg = TEACHER ? &sQ1[0][0] : &sQ2[0][0];  // addressed through xg below (bf16) ...
     const char* qgs = TEACHER ? &sQ1[st][0] : &sQ2[st][0];  // ... or directly (fp32)
-    const SwzAddr<RB1> x1 = ad1.shifted(st * BQ * RB1);
-    const SwzAddr<RB2> x2 = ad2.shifted(st * BQ * RB2);
     const SwzAddr<RBG> xg = adg.shifted(st * BQ * RBG);
 #pragma unroll
     for (int qb = 0; qb < BQ / 32; ++qb) {
@@ -176,20 +172,16 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dk_kerne
       if (MASKED && (kw0 >= p.NK || qb0 >= p.NQ || (CAUSAL && kw0 > qb0 + 31 + off))) continue;  // fully masked
       f32x16 s1 = f32x16{}, s2 = f32x16{};
       __builtin_amdgcn_s_setprio(1);  // MFMA burst at raised priority (as in the forward)
-      if constexpr (EPL == 1) {
-        const int qrow = 32 * qb + prow;
+      // Logit operands: per-chunk LDS offsets left to the compiler (kept as
+      // loop invariants; measured faster here than forming them at each
+      // read), the gradient operands below through SwzAddr.
+      const int qrow = 32 * qb + prow;
 #pragma unroll
-        for (int c = 0; c < NC1; ++c)
-          s1 = M::run(M::load(&sQ1[st][T1::off(qrow, (c * KC + half * EPL) * ESZ)]), kf1[c], s1);
+      for (int c = 0; c < NC1; ++c)
+        s1 = M::run(M::load(&sQ1[st][T1::off(qrow, (c * KC + half * EPL) * ESZ)]), kf1[c], s1);
 #pragma unroll
-        for (int c = 0; c < NC2; ++c)
-          s2 = M::run(M::load(&sQ2[st][T2::off(qrow, (c * KC + half * EPL) * ESZ)]), kf2[c], s2);
-      } else {
-#pragma unroll
-        for (int c = 0; c < NC1; ++c) s1 = M::run(x1.frag(sQ1[0], 32 * qb * RB1, c), kf1[c], s1);
-#pragma unroll
-        for (int c = 0; c < NC2; ++c) s2 = M::run(x2.frag(sQ2[0], 32 * qb * RB2, c), kf2[c], s2);
-      }
+      for (int c = 0; c < NC2; ++c)
+        s2 = M::run(M::load(&sQ2[st][T2::off(qrow, (c * KC + half * EPL) * ESZ)]), kf2[c], s2);
 
       __builtin_amdgcn_s_setprio(0);
       // Registers 8 run .. 8 run + 7 hold rows 32 qb + 16 run + 8 half + 0..7:
