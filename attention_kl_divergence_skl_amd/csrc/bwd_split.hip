@@ -175,13 +175,14 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dk_kerne
       // Logit operands: per-chunk LDS offsets left to the compiler (kept as
       // loop invariants; measured faster here than forming them at each
       // read), the gradient operands below through SwzAddr.
+      // The two chains alternate, so each MFMA's predecessor in its chain is
+      // two issues back.
       const int qrow = 32 * qb + prow;
 #pragma unroll
-      for (int c = 0; c < NC1; ++c)
-        s1 = M::run(M::load(&sQ1[st][T1::off(qrow, (c * KC + half * EPL) * ESZ)]), kf1[c], s1);
-#pragma unroll
-      for (int c = 0; c < NC2; ++c)
-        s2 = M::run(M::load(&sQ2[st][T2::off(qrow, (c * KC + half * EPL) * ESZ)]), kf2[c], s2);
+      for (int c = 0; c < (NC1 > NC2 ? NC1 : NC2); ++c) {
+        if (c < NC1) s1 = M::run(M::load(&sQ1[st][T1::off(qrow, (c * KC + half * EPL) * ESZ)]), kf1[c], s1);
+        if (c < NC2) s2 = M::run(M::load(&sQ2[st][T2::off(qrow, (c * KC + half * EPL) * ESZ)]), kf2[c], s2);
+      }
 
       __builtin_amdgcn_s_setprio(0);
       // Registers 8 run .. 8 run + 7 hold rows 32 qb + 16 run + 8 half + 0..7:
@@ -195,6 +196,16 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dk_kerne
       const int qlim = clamp_i32(p.NQ - qb0), cmin = clamp_i32(key - qb0 - off);
 #pragma unroll
       for (int run = 0; run < 2; ++run) {
+        // Teacher: the gradient operand's transposing reads are issued before
+        // the dS work, so their latency overlaps it (measured 4% on the
+        // teacher kernel; the student kernel, with one more exponential per
+        // element and less room, does better reading them at the MFMAs).
+        frag bq[NCB];
+        if constexpr (TEACHER && EPL != 1) {
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) bq[cb] = xg.trfrag(qg, (32 * qb + run * KC) * RBG, cb);
+          __builtin_amdgcn_sched_barrier(0);
+        }
         float cst[4][8];
 #pragma unroll
         for (int which = 0; which < (TEACHER ? 4 : 3); ++which) {
@@ -231,7 +242,8 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dk_kerne
 #pragma unroll
           for (int e = 0; e < EPL; ++e) a[e] = from_f32<T>(ds[e]);
 #pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) dk[cb] = M::run(a, xg.trfrag(qg, (32 * qb + run * KC) * RBG, cb), dk[cb]);
+          for (int cb = 0; cb < NCB; ++cb)
+            dk[cb] = M::run(a, TEACHER ? bq[cb] : xg.trfrag(qg, (32 * qb + run * KC) * RBG, cb), dk[cb]);
         }
       }
     }
@@ -384,11 +396,10 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kerne
         const int klim = clamp_i32(p.NK - (j0 + kb * 32)), cmax = clamp_i32(qi + off - (j0 + kb * 32));
         const int krow = kb * 32 + prow;
 #pragma unroll
-        for (int c = 0; c < NC1; ++c)
-          s1 = M::run(M::load(&sK1[st][T1::off(krow, (c * KC + half * EPL) * ESZ)]), qf1[c], s1);
-#pragma unroll
-        for (int c = 0; c < NC2; ++c)
-          s2 = M::run(M::load(&sK2[st][T2::off(krow, (c * KC + half * EPL) * ESZ)]), qf2[c], s2);
+        for (int c = 0; c < (NC1 > NC2 ? NC1 : NC2); ++c) {  // chains alternate (see the dK kernel)
+          if (c < NC1) s1 = M::run(M::load(&sK1[st][T1::off(krow, (c * KC + half * EPL) * ESZ)]), qf1[c], s1);
+          if (c < NC2) s2 = M::run(M::load(&sK2[st][T2::off(krow, (c * KC + half * EPL) * ESZ)]), qf2[c], s2);
+        }
         __builtin_amdgcn_s_setprio(0);
         // Registers 8 run .. 8 run + 7 hold keys kb 32 + 16 run + 8 half + 0..7:
         // K chunk `run` (bf16) or chunks 8 run .. 8 run + 7 (fp32) of
