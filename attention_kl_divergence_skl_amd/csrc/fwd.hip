@@ -104,6 +104,7 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(c
 
   const float c1 = p.c1, c2 = p.c2;
   float m1 = neg_inf(), m2 = neg_inf(), l1 = 0.f, l2 = 0.f, acc = 0.f;
+  float mr1 = neg_inf(), mr2 = neg_inf();  // m1 / c1, m2 / c2: running maxima in raw logit units
 
   if (nsteps > 0) fetch(0, kbeg);
   wait_vm();
@@ -159,41 +160,48 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(c
       }
     }
 
-    // Reductions over the 16 values run as 4 independent chains (and a tree
-    // for the max): with two waves per SIMD a single dependent chain of 16
-    // would leave the VALU waiting on its own latency.
-    float px1[4], px2[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      px1[k] = fmaxf(fmaxf(s1[4 * k], s1[4 * k + 1]), fmaxf(s1[4 * k + 2], s1[4 * k + 3]));
-      px2[k] = fmaxf(fmaxf(s2[4 * k], s2[4 * k + 1]), fmaxf(s2[4 * k + 2], s2[4 * k + 3]));
-    }
-    const float mx1 = fmaxf(fmaxf(px1[0], px1[1]), fmaxf(px1[2], px1[3]));
-    const float mx2 = fmaxf(fmaxf(px2[0], px2[1]), fmaxf(px2[2], px2[3]));
-    const float m1n = fmaxf(m1, mx1 * c1), m2n = fmaxf(m2, mx2 * c2);
+    // Block maxima as a tree of 3-input maxima over the 16 logits and the
+    // running maximum, which is kept in raw logit units (mr1, mr2) for that;
+    // the scales are positive, so scaling after the max gives the same value.
+    auto max3 = [](float a, float b, float c) __attribute__((always_inline)) { return fmaxf(fmaxf(a, b), c); };
+    auto tree = [&](const f32x16& v, float mr) __attribute__((always_inline)) {
+      const float b0 = max3(max3(v[0], v[1], v[2]), max3(v[3], v[4], v[5]), max3(v[6], v[7], v[8]));
+      const float b1 = max3(max3(v[9], v[10], v[11]), max3(v[12], v[13], v[14]), v[15]);
+      return max3(b0, b1, mr);
+    };
+    const float mr1n = tree(s1, mr1), mr2n = tree(s2, mr2);
+    const float m1n = mr1n * c1, m2n = mr2n * c2;
     const float m1u = (m1n == neg_inf()) ? 0.f : m1n;  // no key seen yet: keep sums at 0
     const float m2u = (m2n == neg_inf()) ? 0.f : m2n;
     const float a1f = exp2_hw(m1 - m1u), a2f = exp2_hw(m2 - m2u);
 
-    float ps1[4] = {0.f, 0.f, 0.f, 0.f}, ps2[4] = {0.f, 0.f, 0.f, 0.f}, pa[4] = {0.f, 0.f, 0.f, 0.f};
+    // Sums run as 4 independent chains (with two waves per SIMD a single
+    // dependent chain of 16 would leave the VALU waiting on its own latency),
+    // each started by its first term rather than by adding it to zero.
+    float ps1[4], ps2[4], pa[4];
+    auto term = [&](int r, float u1, float u2, float d) __attribute__((always_inline)) {
+      const float e1 = exp2_hw(u1), e2 = exp2_hw(u2);
+      if (r < 4) {
+        ps1[r] = e1;
+        ps2[r] = e2;
+        pa[r] = e1 * d;
+      } else {
+        ps1[r & 3] += e1;
+        ps2[r & 3] += e2;
+        pa[r & 3] = fmaf(e1, d, pa[r & 3]);
+      }
+    };
     if (need_mask) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float u1 = fmaf(s1[r], c1, -m1u), u2 = fmaf(s2[r], c2, -m2u);
-        const float e1 = exp2_hw(u1), e2 = exp2_hw(u2);
-        ps1[r & 3] += e1;
-        ps2[r & 3] += e2;
-        const float d = (s1[r] == neg_inf()) ? 0.f : (u1 - u2);
-        pa[r & 3] = fmaf(e1, d, pa[r & 3]);
+        term(r, u1, u2, (s1[r] == neg_inf()) ? 0.f : (u1 - u2));
       }
     } else {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float u1 = fmaf(s1[r], c1, -m1u), u2 = fmaf(s2[r], c2, -m2u);
-        const float e1 = exp2_hw(u1), e2 = exp2_hw(u2);
-        ps1[r & 3] += e1;
-        ps2[r & 3] += e2;
-        pa[r & 3] = fmaf(e1, u1 - u2, pa[r & 3]);
+        term(r, u1, u2, u1 - u2);
       }
     }
     const float sum1 = (ps1[0] + ps1[1]) + (ps1[2] + ps1[3]);
@@ -205,6 +213,8 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(c
     acc = fmaf(acc, a1f, fmaf(m1u - m2u, sum1, accd));
     m1 = m1n;
     m2 = m2n;
+    mr1 = mr1n;
+    mr2 = mr2n;
   };
 
   // Block-level software pipeline: the MFMAs of the next 32-key block are
