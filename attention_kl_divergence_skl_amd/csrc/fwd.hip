@@ -21,8 +21,9 @@
 // whole key loop; K tiles are loaded straight into LDS (direct-to-LDS loads,
 // XOR-swizzled rows for conflict-free 16-byte reads), shared by the 4 waves and
 // double-buffered: the loads of the next tile are issued before the current
-// one is computed.  The online update runs per 32-key block (one max, two
-// correction factors per block and row), one block behind the MFMAs.
+// one is computed.  The online update runs per 32-key block, one block behind
+// the MFMAs; a block whose terms stay bounded against the current maxima is
+// summed without a new maximum or correction factors (see update below).
 //
 // Split-K (article section "GPU kernel optimisations"): the same kernel over a
 // contiguous key range writes the five per-row partials (m1, l1, m2, l2, acc)
@@ -34,6 +35,13 @@
 #include "skl_internal.h"
 
 namespace skl {
+
+// Running maximum of a row before any of its keys has been seen (base-2 logit
+// units): finite, so shifts and correction factors never form inf - inf, and
+// far enough below any real logit that 2^(t - kNoKey) overflows to +inf.
+constexpr float kNoKey = -1e30f;
+// Largest block sum kept against a stale running maximum (2^64).
+constexpr float kFastCap = 18446744073709551616.0f;
 
 template <typename T, int D1, int D2, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const FwdParams p) {
@@ -103,8 +111,11 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(c
   };
 
   const float c1 = p.c1, c2 = p.c2;
-  float m1 = neg_inf(), m2 = neg_inf(), l1 = 0.f, l2 = 0.f, acc = 0.f;
-  float mr1 = neg_inf(), mr2 = neg_inf();  // m1 / c1, m2 / c2: running maxima in raw logit units
+  // Running maxima in base-2 units start at the finite kNoKey ("no key seen"),
+  // so that every shift and correction factor below is finite; mr1, mr2 are the
+  // maxima of the raw logits (before the scale) over the keys seen so far.
+  float m1 = kNoKey, m2 = kNoKey, l1 = 0.f, l2 = 0.f, acc = 0.f;
+  float mr1 = neg_inf(), mr2 = neg_inf();
 
   if (nsteps > 0) fetch(0, kbeg);
   wait_vm();
@@ -145,7 +156,18 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(c
   };
 
   // Online update of the row statistics with one block whose first key is jb.
-  auto update = [&](f32x16& s1, f32x16& s2, int64_t jb) {
+  //
+  // Most blocks keep the running maxima: the block is first summed against the
+  // current (m1, m2), and that result is kept whenever both of its sums stay at
+  // or below kFastCap = 2^64, which bounds every term by 2^64 (far from fp32
+  // overflow even after summing 2^20 blocks).  A stale maximum only makes the
+  // terms larger, never smaller, so nothing underflows that the exact update
+  // would keep; the sums are the same quantities in another base-2 unit.  Only
+  // when a lane's sums exceed the cap (or no key has been seen yet: m is then
+  // kNoKey and the terms overflow) does that lane take the exact update with a
+  // new block maximum and the correction factors.  The block maximum, the two
+  // correction exponentials and the rescales are thus off the common path.
+  auto update = [&](f32x16& s1, f32x16& s2, int64_t jb) __attribute__((always_inline)) {
     const bool need_mask = (jb + 32 > p.NK) || (CAUSAL && jb + 31 > qw0 + off);
     if (need_mask) {
       // Key jb + ro is visible iff ro < NK - jb and (causal) ro <= qi + off - jb.
@@ -160,61 +182,72 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(c
       }
     }
 
-    // Block maxima as a tree of 3-input maxima over the 16 logits and the
-    // running maximum, which is kept in raw logit units (mr1, mr2) for that;
-    // the scales are positive, so scaling after the max gives the same value.
-    auto max3 = [](float a, float b, float c) __attribute__((always_inline)) { return fmaxf(fmaxf(a, b), c); };
-    auto tree = [&](const f32x16& v, float mr) __attribute__((always_inline)) {
-      const float b0 = max3(max3(v[0], v[1], v[2]), max3(v[3], v[4], v[5]), max3(v[6], v[7], v[8]));
-      const float b1 = max3(max3(v[9], v[10], v[11]), max3(v[12], v[13], v[14]), v[15]);
-      return max3(b0, b1, mr);
-    };
-    const float mr1n = tree(s1, mr1), mr2n = tree(s2, mr2);
-    const float m1n = mr1n * c1, m2n = mr2n * c2;
-    const float m1u = (m1n == neg_inf()) ? 0.f : m1n;  // no key seen yet: keep sums at 0
-    const float m2u = (m2n == neg_inf()) ? 0.f : m2n;
-    const float a1f = exp2_hw(m1 - m1u), a2f = exp2_hw(m2 - m2u);
-
-    // Sums run as 4 independent chains (with two waves per SIMD a single
-    // dependent chain of 16 would leave the VALU waiting on its own latency),
-    // each started by its first term rather than by adding it to zero.
-    float ps1[4], ps2[4], pa[4];
-    auto term = [&](int r, float u1, float u2, float d) __attribute__((always_inline)) {
-      const float e1 = exp2_hw(u1), e2 = exp2_hw(u2);
-      if (r < 4) {
-        ps1[r] = e1;
-        ps2[r] = e2;
-        pa[r] = e1 * d;
+    // Block sums against the shifts (sh1, sh2): sum_k = sum 2^(t_k - sh_k) and
+    // accd = sum 2^(t1 - sh1) * (u1 - u2) with u_k = t_k - sh_k.  They run as 4
+    // independent chains (with two waves per SIMD a single dependent chain of 16
+    // would leave the VALU waiting on its own latency), each started by its
+    // first term rather than by adding it to zero.
+    auto block_sums = [&](float sh1, float sh2, float& sum1, float& sum2, float& accd)
+        __attribute__((always_inline)) {
+      float ps1[4], ps2[4], pa[4];
+      auto term = [&](int r, float u1, float u2, float d) __attribute__((always_inline)) {
+        const float e1 = exp2_hw(u1), e2 = exp2_hw(u2);
+        if (r < 4) {
+          ps1[r] = e1;
+          ps2[r] = e2;
+          pa[r] = e1 * d;
+        } else {
+          ps1[r & 3] += e1;
+          ps2[r & 3] += e2;
+          pa[r & 3] = fmaf(e1, d, pa[r & 3]);
+        }
+      };
+      if (need_mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float u1 = fmaf(s1[r], c1, -sh1), u2 = fmaf(s2[r], c2, -sh2);
+          term(r, u1, u2, (s1[r] == neg_inf()) ? 0.f : (u1 - u2));
+        }
       } else {
-        ps1[r & 3] += e1;
-        ps2[r & 3] += e2;
-        pa[r & 3] = fmaf(e1, d, pa[r & 3]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float u1 = fmaf(s1[r], c1, -sh1), u2 = fmaf(s2[r], c2, -sh2);
+          term(r, u1, u2, u1 - u2);
+        }
       }
+      sum1 = (ps1[0] + ps1[1]) + (ps1[2] + ps1[3]);
+      sum2 = (ps2[0] + ps2[1]) + (ps2[2] + ps2[3]);
+      accd = (pa[0] + pa[1]) + (pa[2] + pa[3]);
     };
-    if (need_mask) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float u1 = fmaf(s1[r], c1, -m1u), u2 = fmaf(s2[r], c2, -m2u);
-        term(r, u1, u2, (s1[r] == neg_inf()) ? 0.f : (u1 - u2));
-      }
+
+    float sum1, sum2, accd;
+    block_sums(m1, m2, sum1, sum2, accd);
+    if (sum1 <= kFastCap && sum2 <= kFastCap) {
+      // t1 - t2 = (u1 - u2) + (m1 - m2): the per-row part is added once per block.
+      l1 += sum1;
+      l2 += sum2;
+      acc += fmaf(m1 - m2, sum1, accd);
     } else {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float u1 = fmaf(s1[r], c1, -m1u), u2 = fmaf(s2[r], c2, -m2u);
-        term(r, u1, u2, u1 - u2);
-      }
+      // Block maxima as a tree of 3-input maxima over the 16 logits and the
+      // running maximum, which is kept in raw logit units (mr1, mr2) for that;
+      // the scales are positive, so scaling after the max gives the same value.
+      auto max3 = [](float a, float b, float c) __attribute__((always_inline)) { return fmaxf(fmaxf(a, b), c); };
+      auto tree = [&](const f32x16& v, float mr) __attribute__((always_inline)) {
+        const float b0 = max3(max3(v[0], v[1], v[2]), max3(v[3], v[4], v[5]), max3(v[6], v[7], v[8]));
+        const float b1 = max3(max3(v[9], v[10], v[11]), max3(v[12], v[13], v[14]), v[15]);
+        return max3(b0, b1, mr);
+      };
+      mr1 = tree(s1, mr1);
+      mr2 = tree(s2, mr2);
+      const float m1n = fmaxf(mr1 * c1, kNoKey), m2n = fmaxf(mr2 * c2, kNoKey);
+      const float a1f = exp2_hw(m1 - m1n), a2f = exp2_hw(m2 - m2n);
+      block_sums(m1n, m2n, sum1, sum2, accd);
+      l1 = fmaf(l1, a1f, sum1);
+      l2 = fmaf(l2, a2f, sum2);
+      acc = fmaf(acc, a1f, fmaf(m1n - m2n, sum1, accd));
+      m1 = m1n;
+      m2 = m2n;
     }
-    const float sum1 = (ps1[0] + ps1[1]) + (ps1[2] + ps1[3]);
-    const float sum2 = (ps2[0] + ps2[1]) + (ps2[2] + ps2[3]);
-    const float accd = (pa[0] + pa[1]) + (pa[2] + pa[3]);
-    // t1 - t2 = (u1 - u2) + (m1u - m2u): the per-row part is added once per block.
-    l1 = fmaf(l1, a1f, sum1);
-    l2 = fmaf(l2, a2f, sum2);
-    acc = fmaf(acc, a1f, fmaf(m1u - m2u, sum1, accd));
-    m1 = m1n;
-    m2 = m2n;
-    mr1 = mr1n;
-    mr2 = mr2n;
   };
 
   // Block-level software pipeline: the MFMAs of the next 32-key block are
@@ -245,10 +278,8 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(c
   const float om2 = __shfl_xor(m2, 32), ol2 = __shfl_xor(l2, 32);
   const float oacc = __shfl_xor(acc, 32);
   const float M1 = fmaxf(m1, om1), M2 = fmaxf(m2, om2);
-  const float M1u = (M1 == neg_inf()) ? 0.f : M1;
-  const float M2u = (M2 == neg_inf()) ? 0.f : M2;
-  const float wa1 = exp2_hw(m1 - M1u), wb1 = exp2_hw(om1 - M1u);
-  const float wa2 = exp2_hw(m2 - M2u), wb2 = exp2_hw(om2 - M2u);
+  const float wa1 = exp2_hw(m1 - M1), wb1 = exp2_hw(om1 - M1);
+  const float wa2 = exp2_hw(m2 - M2), wb2 = exp2_hw(om2 - M2);
   const float L1 = l1 * wa1 + ol1 * wb1;
   const float L2 = l2 * wa2 + ol2 * wb2;
   const float ACC = acc * wa1 + oacc * wb1;
@@ -258,9 +289,10 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(c
       const int64_t BH = gridDim.x / ((int64_t)p.num_qtiles * p.splits);
       const int64_t stride_f = BH * p.splits * p.NQ;
       float* dst = p.part + (bh * p.splits + split) * p.NQ + qi;
-      dst[0] = M1;
+      // A split in which the row saw no key writes (-inf, 0, -inf, 0, 0).
+      dst[0] = (L1 > 0.f) ? M1 : neg_inf();
       dst[stride_f] = L1;
-      dst[2 * stride_f] = M2;
+      dst[2 * stride_f] = (L2 > 0.f) ? M2 : neg_inf();
       dst[3 * stride_f] = L2;
       dst[4 * stride_f] = ACC;
     } else {

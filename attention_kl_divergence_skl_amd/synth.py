@@ -39,12 +39,17 @@ class Recipe:
                    (needs d1 == d2); then Q1 *= amp1, Q2 *= amp2.
       "identical"  Q2 = Q1 and K2 = K1 (bitwise), Q1 *= amp1 first.
       "uniform1"   like "iid" but Q1 = 0, so the teacher rows are uniform.
+
+    kramp > 0 then scales key row j of K1 and K2 by 1 + kramp * j / (NK - 1),
+    so logits grow along the key axis and later keys overtake every earlier
+    row maximum by a wide margin.
     """
 
     kind: str = "iid"
     noise: float = 0.0
     amp1: float = 1.0
     amp2: float = 1.0
+    kramp: float = 0.0
 
 
 @dataclasses.dataclass(frozen=True)
@@ -156,6 +161,10 @@ def head_inputs(w: Workload, b: int, h: int) -> Tuple[np.ndarray, np.ndarray, np
         q1 = q1 * np.float32(r.amp1)
     if r.amp2 != 1.0 and r.kind != "identical":
         q2 = q2 * np.float32(r.amp2)
+    if r.kramp:
+        ramp = (1.0 + r.kramp * np.arange(w.NK) / max(w.NK - 1, 1)).astype(np.float32)[:, None]
+        k1 = k1 * ramp
+        k2 = k2 * ramp if r.kind != "identical" else k1
     if r.kind == "identical":
         q1 = round_to_dtype(q1, w.dtype)
         k1 = round_to_dtype(k1, w.dtype)

@@ -149,6 +149,33 @@ def test_underflowing_probabilities_stay_finite(gpu_lib, causal):
         check_grad(f"peaked dK ({setting})", w, grad_to_np(dk), rk)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_rising_logits_overtake_running_max(gpu_lib, causal):
+    """Key norms grow along the key axis, so late keys overtake each row's
+    running maximum by far more than 2^64 in base-2 terms: the forward must
+    leave its kept-maximum sums for the exact update with new maxima and
+    correction factors, many times per row.  (bf16 only: LSE reaches ~220
+    nats here, where one fp32 ulp exceeds the fp32 LSE tolerance.)"""
+    w = W("rising_bf16", 1, 2, 256, 640, 64, 64, "bf16", causal,
+          synth.Recipe("iid", amp1=6.0, amp2=6.0, kramp=8.0))
+    say(f"[rising logits] {w.name} causal={causal}")
+    x, t = to_device(w)
+    # The inputs really do that: base-2 logits of the first 32 keys against the row maximum.
+    s1 = (x["q1"][0, 0].astype(np.float64) @ x["k1"][0, 0].astype(np.float64).T) * w.scale1 / np.log(2)
+    if causal:
+        s1 = np.where(np.arange(w.NK)[None, :] <= np.arange(w.NQ)[:, None] + (w.NK - w.NQ), s1, -np.inf)
+    gap = s1.max(axis=1) - s1[:, :32].max(axis=1)
+    assert np.mean(gap > 80) > 0.9, "recipe must move the row maximum far past the first block's"
+    got, (kl, l1, l2) = gpu_forward(gpu_lib, w, t)
+    check_rows(w.name, w, got, oracle_forward(w, x))
+    dq, dk = gpu_lib.skl_backward_student(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, t["g"],
+                                          w.scale1, w.scale2, w.causal)
+    torch.cuda.synchronize()
+    rq, rk = oracle_backward(w, x, "student")
+    check_grad(f"{w.name} dQ2", w, grad_to_np(dq), rq)
+    check_grad(f"{w.name} dK2", w, grad_to_np(dk), rk)
+
+
 @pytest.mark.parametrize("splits", [1, 2, 3, 4, 8])
 @pytest.mark.parametrize("causal", [False, True])
 def test_splitk_matches_oracle_and_plain_forward(gpu_lib, splits, causal):
