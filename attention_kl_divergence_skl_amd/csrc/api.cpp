@@ -74,8 +74,9 @@ skl_status check_shape(const skl_shape* s, bool need_nk) {
     return fail(SKL_ERR_UNSUPPORTED, "head dims d1=%d d2=%d (supported: 64, 128)", s->d1, s->d2);
   if (s->NK == 0 && s->NQ > 0 && s->B > 0 && s->H > 0)
     return fail(SKL_ERR_INVALID_ARGUMENT, "N_K = 0 with N_Q > 0: empty softmax");
-  // Index arithmetic inside the kernels: grid sizes fit in 32 bits.
-  if (s->NQ > (int64_t(1) << 31) || s->NK > (int64_t(1) << 31) || s->B * s->H > (int64_t(1) << 31))
+  // Index arithmetic inside the kernels: grid sizes fit in 32 bits, and row
+  // indices (plus a tile) in 31.
+  if (s->NQ >= (int64_t(1) << 30) || s->NK >= (int64_t(1) << 30) || s->B * s->H > (int64_t(1) << 31))
     return fail(SKL_ERR_UNSUPPORTED, "sizes too large");
   const int64_t mult = s->dtype == SKL_BF16 ? 8 : 4;
   const int64_t* all[4] = {s->sq1, s->sk1, s->sq2, s->sk2};

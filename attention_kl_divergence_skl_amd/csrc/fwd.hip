@@ -93,29 +93,34 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(c
   for (int c = 0; c < NC2; ++c)
     qf2[c] = qvalid ? M::load(q2p + (qi * p.sq2.n + c * KC + half * EPL) * ESZ) : M::zero();
 
-  // Key range of this workgroup.
-  int64_t kbeg = 0, kend = p.NK;
-  if (CAUSAL) kend = min(kend, (int64_t)(qt + 1) * kFwdBQ + off);
+  // Key range of this workgroup and the loop's bounds, all wave-uniform and
+  // in 32-bit scalar arithmetic (the host keeps N_Q and N_K below 2^30).
+  const int NK = (int)p.NK, offk = (int)off;
+  const int qw0s = qt * kFwdBQ + wave * 32;  // first query of this wave
+  int kbeg = 0, kend = NK;
+  if (CAUSAL) kend = min(kend, (qt + 1) * kFwdBQ + offk);
   if (SPLIT) {
-    kbeg = (int64_t)split * p.split_len;
-    kend = min(kend, kbeg + (int64_t)p.split_len);
+    kbeg = split * p.split_len;
+    kend = min(kend, kbeg + p.split_len);
   }
-  const int64_t nsteps = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
-  const int64_t wave_kmax = CAUSAL ? qw0 + 31 + off : p.NK - 1;  // last key any row of the wave sees
+  const int nsteps = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+  const int wave_kmax = CAUSAL ? qw0s + 31 + offk : NK - 1;  // last key any row of the wave sees
+  // A 32-key block starting at jb needs the mask iff it reaches past the last
+  // key or (causal) past the diagonal of the wave's first row: jb > mask_after.
+  const int mask_after = CAUSAL ? min(NK - 32, qw0s + offk - 31) : NK - 32;
 
   // Key tiles are loaded straight into a double-buffered LDS ring: the loads
   // of tile i+1 are in flight while tile i is computed; one barrier per tile.
-  auto fetch = [&](int st, int64_t j0) {
-    tile_load_async<BK, RB1>(sK1[st], k1p, p.sk1.n * ESZ, j0, p.NK, wave, lane);
-    tile_load_async<BK, RB2>(sK2[st], k2p, p.sk2.n * ESZ, j0, p.NK, wave, lane);
+  const int64_t rs1 = p.sk1.n * ESZ, rs2 = p.sk2.n * ESZ;
+  auto fetch = [&](int st, int j0) {
+    tile_load_async<BK, RB1>(sK1[st], k1p, rs1, j0, p.NK, wave, lane);
+    tile_load_async<BK, RB2>(sK2[st], k2p, rs2, j0, p.NK, wave, lane);
   };
 
   const float c1 = p.c1, c2 = p.c2;
   // Running maxima in base-2 units start at the finite kNoKey ("no key seen"),
-  // so that every shift and correction factor below is finite; mr1, mr2 are the
-  // maxima of the raw logits (before the scale) over the keys seen so far.
+  // so that every shift and correction factor below is finite.
   float m1 = kNoKey, m2 = kNoKey, l1 = 0.f, l2 = 0.f, acc = 0.f;
-  float mr1 = neg_inf(), mr2 = neg_inf();
 
   if (nsteps > 0) fetch(0, kbeg);
   wait_vm();
@@ -167,11 +172,11 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(c
   // kNoKey and the terms overflow) does that lane take the exact update with a
   // new block maximum and the correction factors.  The block maximum, the two
   // correction exponentials and the rescales are thus off the common path.
-  auto update = [&](f32x16& s1, f32x16& s2, int64_t jb) __attribute__((always_inline)) {
-    const bool need_mask = (jb + 32 > p.NK) || (CAUSAL && jb + 31 > qw0 + off);
+  auto update = [&](f32x16& s1, f32x16& s2, int jb) __attribute__((always_inline)) {
+    const bool need_mask = jb > mask_after;
     if (need_mask) {
       // Key jb + ro is visible iff ro < NK - jb and (causal) ro <= qi + off - jb.
-      const int klim = clamp_i32(p.NK - jb), cmax = clamp_i32(qi + off - jb);
+      const int klim = NK - jb, cmax = (int)qi + offk - jb;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int ro = acc_row(r, half);
@@ -228,18 +233,16 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(c
       l2 += sum2;
       acc += fmaf(m1 - m2, sum1, accd);
     } else {
-      // Block maxima as a tree of 3-input maxima over the 16 logits and the
-      // running maximum, which is kept in raw logit units (mr1, mr2) for that;
-      // the scales are positive, so scaling after the max gives the same value.
+      // Block maxima of the raw logits as a tree of 3-input maxima, scaled
+      // afterwards (the scales are positive) and joined with the running
+      // maxima; a lane whose keys are all masked keeps its maxima.
       auto max3 = [](float a, float b, float c) __attribute__((always_inline)) { return fmaxf(fmaxf(a, b), c); };
-      auto tree = [&](const f32x16& v, float mr) __attribute__((always_inline)) {
+      auto tree = [&](const f32x16& v) __attribute__((always_inline)) {
         const float b0 = max3(max3(v[0], v[1], v[2]), max3(v[3], v[4], v[5]), max3(v[6], v[7], v[8]));
         const float b1 = max3(max3(v[9], v[10], v[11]), max3(v[12], v[13], v[14]), v[15]);
-        return max3(b0, b1, mr);
+        return fmaxf(b0, b1);
       };
-      mr1 = tree(s1, mr1);
-      mr2 = tree(s2, mr2);
-      const float m1n = fmaxf(mr1 * c1, kNoKey), m2n = fmaxf(mr2 * c2, kNoKey);
+      const float m1n = fmaxf(tree(s1) * c1, m1), m2n = fmaxf(tree(s2) * c2, m2);
       const float a1f = exp2_hw(m1 - m1n), a2f = exp2_hw(m2 - m2n);
       block_sums(m1n, m2n, sum1, sum2, accd);
       l1 = fmaf(l1, a1f, sum1);
@@ -255,9 +258,9 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(c
   // barrier too), so each wave keeps matrix work in flight while its VALU
   // runs the softmax.  Blocks past the wave's last visible key are skipped.
   f32x16 sa1, sa2, sb1, sb2;  // block 0 / block 1 of the current tile
-  auto step = [&](auto stc, int64_t it) {
+  auto step = [&](auto stc, int it) {
     constexpr int st = decltype(stc)::value;
-    const int64_t j0 = kbeg + it * BK;
+    const int j0 = kbeg + it * BK;
     if (it + 1 < nsteps) fetch(st ^ 1, j0 + BK);
     const bool live0 = j0 <= wave_kmax, live1 = j0 + 32 <= wave_kmax;
     if (live1) logits(stc, 1, sb1, sb2);
@@ -268,7 +271,7 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(c
     if (live1) update(sb1, sb2, j0 + 32);
   };
   if (nsteps > 0 && kbeg <= wave_kmax) logits(std::integral_constant<int, 0>{}, 0, sa1, sa2);
-  for (int64_t it = 0; it < nsteps; it += 2) {
+  for (int it = 0; it < nsteps; it += 2) {
     step(std::integral_constant<int, 0>{}, it);
     if (it + 1 < nsteps) step(std::integral_constant<int, 1>{}, it + 1);
   }
