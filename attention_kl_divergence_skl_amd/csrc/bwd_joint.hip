@@ -109,8 +109,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_joint_dk_kernel(const BwdPara
 
   float pv = 0.f;
   auto fetch = [&](int st, int64_t q0) {
-    tile_load_async<BQ, RB1>(sQ1[st], q1p, p.sq1.n * ESZ, q0, p.NQ, wave, lane);
-    tile_load_async<BQ, RB2>(sQ2[st], q2p, p.sq2.n * ESZ, q0, p.NQ, wave, lane);
+    tile_load_async<BQ, RB1>(sQ1[st], q1p, p.sq1.n * ESZ, (int)q0, (int)p.NQ, wave, lane);
+    tile_load_async<BQ, RB2>(sQ2[st], q2p, p.sq2.n * ESZ, (int)q0, (int)p.NQ, wave, lane);
     pv = 0.f;
     if (tid < 4 * BQ) {
       const int which = tid / BQ, row = tid % BQ;
@@ -334,8 +334,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_joint_dq_kernel(const BwdPara
   const int64_t wave_kmax = CAUSAL ? qw0 + 31 + off : p.NK - 1;
 
   auto fetch = [&](int st, int64_t j0) {
-    tile_load_async<BK, RB1>(sK1[st], k1p, p.sk1.n * ESZ, j0, p.NK, wave, lane);
-    tile_load_async<BK, RB2>(sK2[st], k2p, p.sk2.n * ESZ, j0, p.NK, wave, lane);
+    tile_load_async<BK, RB1>(sK1[st], k1p, p.sk1.n * ESZ, (int)j0, (int)p.NK, wave, lane);
+    tile_load_async<BK, RB2>(sK2[st], k2p, p.sk2.n * ESZ, (int)j0, (int)p.NK, wave, lane);
   };
 
   if (nsteps > 0) fetch(0, 0);

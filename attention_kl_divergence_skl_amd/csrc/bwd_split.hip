@@ -122,8 +122,8 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dk_kerne
   // register per thread.
   float pv = 0.f;
   auto fetch = [&](int st, int64_t q0) {
-    tile_load_async<BQ, RB1>(sQ1[st], q1p, p.sq1.n * ESZ, q0, p.NQ, wave, lane);
-    tile_load_async<BQ, RB2>(sQ2[st], q2p, p.sq2.n * ESZ, q0, p.NQ, wave, lane);
+    tile_load_async<BQ, RB1>(sQ1[st], q1p, p.sq1.n * ESZ, (int)q0, (int)p.NQ, wave, lane);
+    tile_load_async<BQ, RB2>(sQ2[st], q2p, p.sq2.n * ESZ, (int)q0, (int)p.NQ, wave, lane);
     pv = 0.f;
     if (tid < 4 * BQ) {
       const int which = tid / BQ, row = tid % BQ;
@@ -307,10 +307,13 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kerne
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int half = lane >> 5, col = lane & 31;
 
-  const int num_qtiles = (int)((p.NQ + BQ - 1) / BQ);
+  // Row and key indices are 32-bit (the host keeps N_Q and N_K below 2^30),
+  // so the loop control below is scalar arithmetic.
+  const int NQ = (int)p.NQ, NK = (int)p.NK;
+  const int num_qtiles = (NQ + BQ - 1) / BQ;
   int64_t t = xcd_remap(blockIdx.x, gridDim.x);
   int split = 0;  // key range of this workgroup when the keys are split (few query tiles)
   if (p.dq_splits > 1) {
@@ -321,10 +324,10 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kerne
   int qt = (int)(t % num_qtiles);
   if (CAUSAL) qt = num_qtiles - 1 - qt;  // longest rows first
   const int64_t b = bh / p.H, h = bh % p.H;
-  const int64_t off = p.NK - p.NQ;
-  const int64_t qw0 = (int64_t)qt * BQ + 32 * wave;
-  const int64_t qi = qw0 + col;
-  const bool qvalid = qi < p.NQ;
+  const int off = NK - NQ;
+  const int qw0 = qt * BQ + 32 * wave;
+  const int qi = qw0 + col;
+  const bool qvalid = qi < NQ;
 
   const char* const q1p = (const char*)p.q1 + (b * p.sq1.b + h * p.sq1.h) * ESZ;
   const char* const q2p = (const char*)p.q2 + (b * p.sq2.b + h * p.sq2.h) * ESZ;
@@ -334,10 +337,10 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kerne
   frag qf1[NC1], qf2[NC2];
 #pragma unroll
   for (int c = 0; c < NC1; ++c)
-    qf1[c] = qvalid ? M::load(q1p + (qi * p.sq1.n + c * KC + half * EPL) * ESZ) : M::zero();
+    qf1[c] = qvalid ? M::load(q1p + ((int64_t)qi * p.sq1.n + c * KC + half * EPL) * ESZ) : M::zero();
 #pragma unroll
   for (int c = 0; c < NC2; ++c)
-    qf2[c] = qvalid ? M::load(q2p + (qi * p.sq2.n + c * KC + half * EPL) * ESZ) : M::zero();
+    qf2[c] = qvalid ? M::load(q2p + ((int64_t)qi * p.sq2.n + c * KC + half * EPL) * ESZ) : M::zero();
 
   // Per-row constants: this lane's query row.
   float L1 = 0.f, L2 = 0.f, ga = 0.f, gb = 0.f;
@@ -353,18 +356,18 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kerne
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) dq[cb] = f32x16{};
 
-  int64_t kbeg = 0, kend = p.NK;
-  if (CAUSAL) kend = min(kend, (int64_t)(qt + 1) * BQ + off);
+  int kbeg = 0, kend = NK;
+  if (CAUSAL) kend = min(kend, (qt + 1) * BQ + off);
   if (p.dq_splits > 1) {
-    kbeg = (int64_t)split * p.dq_split_len;
-    kend = min(kend, kbeg + (int64_t)p.dq_split_len);
+    kbeg = split * p.dq_split_len;
+    kend = min(kend, kbeg + p.dq_split_len);
   }
-  const int64_t nsteps = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
-  const int64_t wave_kmax = CAUSAL ? qw0 + 31 + off : p.NK - 1;
+  const int nsteps = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+  const int wave_kmax = CAUSAL ? qw0 + 31 + off : NK - 1;
 
-  auto fetch = [&](int st, int64_t j0) {
-    tile_load_async<BK, RB1>(sK1[st], k1p, p.sk1.n * ESZ, j0, p.NK, wave, lane);
-    tile_load_async<BK, RB2>(sK2[st], k2p, p.sk2.n * ESZ, j0, p.NK, wave, lane);
+  auto fetch = [&](int st, int j0) {
+    tile_load_async<BK, RB1>(sK1[st], k1p, p.sk1.n * ESZ, j0, NK, wave, lane);
+    tile_load_async<BK, RB2>(sK2[st], k2p, p.sk2.n * ESZ, j0, NK, wave, lane);
   };
 
   if (nsteps > 0) fetch(0, kbeg);
@@ -375,15 +378,14 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kerne
 
   // One key step (64 keys).  MASKED steps are those that reach the causal
   // diagonal of some wave or a ragged edge; the others carry no mask code.
-  auto step = [&](auto masked, int64_t it) __attribute__((always_inline)) {
+  auto step = [&](auto masked, int it) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked)::value;
-    const int st = (int)(it & 1);
-    const int64_t j0 = kbeg + it * BK;
+    const int st = it & 1;
+    const int j0 = kbeg + it * BK;
     if (it + 1 < nsteps) fetch(st ^ 1, j0 + BK);
 
-    if (!MASKED || wave_uniform(j0 <= wave_kmax)) {
-      const bool need_mask =
-          MASKED && wave_uniform((j0 + BK > p.NK) || (CAUSAL && j0 + BK - 1 > qw0 + off) || (qw0 + 32 > p.NQ));
+    if (!MASKED || j0 <= wave_kmax) {
+      const bool need_mask = MASKED && ((j0 + BK > NK) || (CAUSAL && j0 + BK - 1 > qw0 + off) || (qw0 + 32 > NQ));
       // (Here the per-chunk LDS offsets are left to the compiler, which keeps
       // them as loop invariants: measured faster than forming them at each
       // read as the dK kernel does.)
@@ -393,7 +395,7 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kerne
         f32x16 s1 = f32x16{}, s2 = f32x16{};
         __builtin_amdgcn_s_setprio(1);  // MFMA burst at raised priority (as in the forward)
         // Key j0 + 32 kb + ro is visible iff ro < NK - jb and (causal) ro <= qi + off - jb.
-        const int klim = clamp_i32(p.NK - (j0 + kb * 32)), cmax = clamp_i32(qi + off - (j0 + kb * 32));
+        const int klim = NK - (j0 + kb * 32), cmax = qi + off - (j0 + kb * 32);
         const int krow = kb * 32 + prow;
 #pragma unroll
         for (int c = 0; c < (NC1 > NC2 ? NC1 : NC2); ++c) {  // chains alternate (see the dK kernel)
@@ -446,13 +448,13 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kerne
   // qt 128 + off - 63) or the ragged key edge; a ragged query tile masks all.
   // Both conditions hold from some step on; first_ge(x) is the first step
   // whose first key is >= x.
-  auto first_ge = [&](int64_t x) -> int64_t { return x <= kbeg ? 0 : (x - kbeg + BK - 1) / BK; };
-  int64_t tail = 0;
-  if ((int64_t)qt * BQ + BQ <= p.NQ) {
-    tail = min(nsteps, first_ge(p.NK - BK + 1));
-    if (CAUSAL) tail = min(tail, first_ge((int64_t)qt * BQ + off - BK + 2));
+  auto first_ge = [&](int x) -> int { return x <= kbeg ? 0 : (x - kbeg + BK - 1) / BK; };
+  int tail = 0;
+  if (qt * BQ + BQ <= NQ) {
+    tail = min(nsteps, first_ge(NK - BK + 1));
+    if (CAUSAL) tail = min(tail, first_ge(qt * BQ + off - BK + 2));
   }
-  int64_t it = 0;
+  int it = 0;
   for (; it < tail; ++it) step(std::false_type{}, it);
   for (; it < nsteps; ++it) step(std::true_type{}, it);
 

@@ -113,8 +113,8 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(c
   // of tile i+1 are in flight while tile i is computed; one barrier per tile.
   const int64_t rs1 = p.sk1.n * ESZ, rs2 = p.sk2.n * ESZ;
   auto fetch = [&](int st, int j0) {
-    tile_load_async<BK, RB1>(sK1[st], k1p, rs1, j0, p.NK, wave, lane);
-    tile_load_async<BK, RB2>(sK2[st], k2p, rs2, j0, p.NK, wave, lane);
+    tile_load_async<BK, RB1>(sK1[st], k1p, rs1, j0, NK, wave, lane);
+    tile_load_async<BK, RB2>(sK2[st], k2p, rs2, j0, NK, wave, lane);
   };
 
   const float c1 = p.c1, c2 = p.c2;

@@ -123,16 +123,16 @@ struct SwzTile {
 // data is in LDS once each wave has waited for its loads (vmcnt 0) and the
 // workgroup has passed a barrier.
 template <int ROWS, int ROWB>
-__device__ __forceinline__ void tile_load_async(char* tile, const char* g, int64_t rs, int64_t j0, int64_t nrows,
-                                                int wave, int lane) {
+__device__ __forceinline__ void tile_load_async(char* tile, const char* g, int64_t rs, int j0, int nrows, int wave,
+                                                int lane) {
   using TL = SwzTile<ROWB>;
   constexpr int RPI = 1024 / ROWB;      // rows per wave instruction
   constexpr int NI = ROWS / RPI;        // instructions per tile
   static_assert(NI % 4 == 0, "tile must split evenly over 4 waves");
   // Uniform 64-bit row base plus a 32-bit per-lane offset (the host keeps
-  // ROWS * rs below 2^31).
-  const char* const base = g + j0 * rs;
-  const int rmax = (int)(nrows - 1 - j0 < ROWS - 1 ? nrows - 1 - j0 : ROWS - 1);
+  // ROWS * rs below 2^31, and row indices below 2^30).
+  const char* const base = g + (int64_t)j0 * rs;
+  const int rmax = nrows - 1 - j0 < ROWS - 1 ? nrows - 1 - j0 : ROWS - 1;
   const int pc = lane % TL::CPR;
   const int irs = (int)rs;
 #pragma unroll
