@@ -227,12 +227,9 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(c
 
     float sum1, sum2, accd;
     block_sums(m1, m2, sum1, sum2, accd);
-    if (sum1 <= kFastCap && sum2 <= kFastCap) {
-      // t1 - t2 = (u1 - u2) + (m1 - m2): the per-row part is added once per block.
-      l1 += sum1;
-      l2 += sum2;
-      acc += fmaf(m1 - m2, sum1, accd);
-    } else {
+    // t1 - t2 = (u1 - u2) + (m1 - m2): the per-row part is added once per block.
+    float nl1 = l1 + sum1, nl2 = l2 + sum2, nacc = acc + fmaf(m1 - m2, sum1, accd);
+    if (!(sum1 <= kFastCap && sum2 <= kFastCap)) {
       // Block maxima of the raw logits as a tree of 3-input maxima, scaled
       // afterwards (the scales are positive) and joined with the running
       // maxima; a lane whose keys are all masked keeps its maxima.
@@ -245,12 +242,15 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(c
       const float m1n = fmaxf(tree(s1) * c1, m1), m2n = fmaxf(tree(s2) * c2, m2);
       const float a1f = exp2_hw(m1 - m1n), a2f = exp2_hw(m2 - m2n);
       block_sums(m1n, m2n, sum1, sum2, accd);
-      l1 = fmaf(l1, a1f, sum1);
-      l2 = fmaf(l2, a2f, sum2);
-      acc = fmaf(acc, a1f, fmaf(m1n - m2n, sum1, accd));
+      nl1 = fmaf(l1, a1f, sum1);
+      nl2 = fmaf(l2, a2f, sum2);
+      nacc = fmaf(acc, a1f, fmaf(m1n - m2n, sum1, accd));
       m1 = m1n;
       m2 = m2n;
     }
+    l1 = nl1;
+    l2 = nl2;
+    acc = nacc;
   };
 
   // Block-level software pipeline: the MFMAs of the next 32-key block are
