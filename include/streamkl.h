@@ -36,6 +36,8 @@
  *   reported by the HIP runtime returns SKL_ERR_HIP.
  * - Sizes of zero (B, H or N_Q) are valid and enqueue nothing.  N_K = 0 with
  *   N_Q > 0 is invalid (an empty softmax).
+ * - N_Q and N_K must be below 2^30 and B * H at most 2^31 (row indices are
+ *   32-bit inside the kernels); larger sizes return SKL_ERR_UNSUPPORTED.
  * - Alignment: data pointers 16-byte aligned; b/h/n strides multiples of 8
  *   elements (bf16) or 4 elements (fp32).  Supported head dims: 64 and 128.
  * - Outputs must not alias inputs.

@@ -73,6 +73,8 @@ def _fwd(lib, s, scale1=0.1, scale2=0.1, causal=0, ptrs=None, outs=(A + 0x4000, 
     (lambda s: s.sq1.__setitem__(2, 100), UNSUPPORTED),   # n stride not a multiple of 8 bf16 elements
     (lambda s: s.sk2.__setitem__(0, -8), INVALID),
     (lambda s: s.sq2.__setitem__(2, 1 << 24), UNSUPPORTED),   # 64 rows of this stride overflow 32-bit offsets
+    (lambda s: setattr(s, "NK", 1 << 30), UNSUPPORTED),       # row indices are 32-bit in the kernels
+    (lambda s: setattr(s, "NQ", 1 << 30), UNSUPPORTED),
 ])
 def test_forward_rejects_bad_shapes(lib, mut, expect):
     s = _shape()
