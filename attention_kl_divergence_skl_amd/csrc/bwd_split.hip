@@ -157,8 +157,8 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dk_kerne
   // MASKED steps are those whose 64 x 128 (query, key) rectangle reaches past
   // the causal diagonal or a ragged edge, decided from workgroup-uniform
   // values, so the common unmasked step carries no mask code at all.
-  auto step = [&](auto masked, int64_t it) __attribute__((always_inline)) {
-    const int st = (int)(it & 1);
+  auto step = [&](auto masked, auto stc, int64_t it) __attribute__((always_inline)) {
+    const int st = stc;  // it & 1; a compile-time constant in the unrolled mask-free loop
     constexpr bool MASKED = decltype(masked)::value;
     const int64_t q0 = qbeg + it * BQ;
     if (it + 1 < nsteps) fetch(st ^ 1, q0 + BQ);  // next tile in flight during this step
@@ -263,9 +263,22 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dk_kerne
     if (p.NQ % BQ != 0) tail = max(head, nsteps - 1);
   }
   int64_t it = 0;
-  for (; it < head; ++it) step(std::true_type{}, it);
-  for (; it < tail; ++it) step(std::false_type{}, it);
-  for (; it < nsteps; ++it) step(std::true_type{}, it);
+  for (; it < head; ++it) step(std::true_type{}, (int)(it & 1), it);
+  // Mask-free steps in stage pairs: the LDS stage is then a constant and
+  // folds into the immediate offset of every LDS read.
+  if (it < tail && (it & 1)) {
+    step(std::false_type{}, 1, it);
+    ++it;
+  }
+  for (; it + 1 < tail; it += 2) {
+    step(std::false_type{}, std::integral_constant<int, 0>{}, it);
+    step(std::false_type{}, std::integral_constant<int, 1>{}, it + 1);
+  }
+  if (it < tail) {
+    step(std::false_type{}, 0, it);
+    ++it;
+  }
+  for (; it < nsteps; ++it) step(std::true_type{}, (int)(it & 1), it);
 
   char* const dkp = (char*)p.dk + (b * p.sdk.b + h * p.sdk.h) * ESZ;
 #pragma unroll
@@ -378,9 +391,9 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kerne
 
   // One key step (64 keys).  MASKED steps are those that reach the causal
   // diagonal of some wave or a ragged edge; the others carry no mask code.
-  auto step = [&](auto masked, int it) __attribute__((always_inline)) {
+  auto step = [&](auto masked, auto stc, int it) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked)::value;
-    const int st = it & 1;
+    const int st = stc;  // it & 1; a compile-time constant in the unrolled mask-free loop
     const int j0 = kbeg + it * BK;
     if (it + 1 < nsteps) fetch(st ^ 1, j0 + BK);
 
@@ -455,8 +468,16 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kerne
     if (CAUSAL) tail = min(tail, first_ge(qt * BQ + off - BK + 2));
   }
   int it = 0;
-  for (; it < tail; ++it) step(std::false_type{}, it);
-  for (; it < nsteps; ++it) step(std::true_type{}, it);
+  // Mask-free steps in stage pairs (the LDS stage folds into the read offsets).
+  for (; it + 1 < tail; it += 2) {
+    step(std::false_type{}, std::integral_constant<int, 0>{}, it);
+    step(std::false_type{}, std::integral_constant<int, 1>{}, it + 1);
+  }
+  if (it < tail) {
+    step(std::false_type{}, 0, it);
+    ++it;
+  }
+  for (; it < nsteps; ++it) step(std::true_type{}, it & 1, it);
 
   // dQ of this wave's rows: accumulator register r holds query qw0 + acc_row(r, half).
   if (p.dq_splits > 1) {
