@@ -37,7 +37,8 @@ namespace skl {
 
 namespace {
 
-// dS of one accumulator element from the two logits (raw dot products) and
+// dS of one accumulator element (dK kernel, whose accumulator rows are queries
+// with their own g) from the two logits (raw dot products) and
 // the row constants L_k = LSE_k log2 e and, for the student, ga = g; for the
 // teacher ga = g ln2 and gb = g KL, so that
 //   student: g (P2 - P1)                      = ga (2^u2 - 2^u1)
@@ -49,6 +50,42 @@ __device__ __forceinline__ float dS_of(float s1, float s2, float c1, float c2, f
   const float u2 = fmaf(s2, c2, -L2);
   if (TEACHER) return exp2_hw(u1) * fmaf(ga, u1 - u2, -gb);
   return ga * (exp2_hw(u2) - exp2_hw(u1));
+}
+
+// sign(g) dS of one accumulator element (dQ kernel, one query per lane) from
+// the two logits (raw dot products) and two row constants that fold the upstream gradient into the exponents.  With
+// u_k = t_k - LSE_k log2 e (so P_k = 2^u_k), ga = g (student) or g ln2
+// (teacher) and k = log2 |ga|:
+//   student: g (P2 - P1) = sign(g) (2^(u2 + k) - 2^(u1 + k))
+//   teacher: g P1 (ln2 (u1 - u2) - KL)
+//              = sign(g) 2^(u1 + k) ((u1 + k) - (u2 + k + KL log2 e))
+// so the row constants are A1 = L1 - k and A2 = L2 - k (student) or
+// L2 - k - KL log2 e (teacher), and the element needs no multiply by g.  A
+// row with g = 0 gets A1 = kZeroRow (and a finite A2), whose exponential is 0.
+// The dQ kernel applies the sign to each finished dQ row.
+template <bool TEACHER>
+__device__ __forceinline__ float dS_abs(float s1, float s2, float c1, float c2, float A1, float A2) {
+  const float w1 = fmaf(s1, c1, -A1);
+  const float w2 = fmaf(s2, c2, -A2);
+  if (TEACHER) return exp2_hw(w1) * (w1 - w2);
+  return exp2_hw(w2) - exp2_hw(w1);
+}
+
+constexpr float kZeroRow = 1e30f;
+
+// Row constants of dS_abs from the saved row values (natural-log LSEs, KL and
+// g); valid rows only.
+template <bool TEACHER>
+__device__ __forceinline__ void row_consts(float lse1, float lse2, float kl, float g, float& A1, float& A2) {
+  const float ga = TEACHER ? g * kLn2 : g;
+  if (ga == 0.f) {
+    A1 = kZeroRow;
+    A2 = TEACHER ? 0.f : kZeroRow;
+    return;
+  }
+  const float k = log2f(fabsf(ga));
+  A1 = fmaf(lse1, kLog2e, -k);
+  A2 = TEACHER ? fmaf(lse2 - kl, kLog2e, -k) : fmaf(lse2, kLog2e, -k);
 }
 
 }  // namespace
@@ -355,14 +392,12 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kerne
   for (int c = 0; c < NC2; ++c)
     qf2[c] = qvalid ? M::load(q2p + ((int64_t)qi * p.sq2.n + c * KC + half * EPL) * ESZ) : M::zero();
 
-  // Per-row constants: this lane's query row.
-  float L1 = 0.f, L2 = 0.f, ga = 0.f, gb = 0.f;
+  // Row constants of this lane's query row (see dS_abs).  The sign of g is
+  // applied to the finished dQ row instead of to every element.
+  float A1 = kZeroRow, A2 = TEACHER ? 0.f : kZeroRow;
   if (qvalid) {
     const int64_t o = bh * p.NQ + qi;
-    L1 = p.lse1[o] * kLog2e;
-    L2 = p.lse2[o] * kLog2e;
-    ga = TEACHER ? p.dkl[o] * kLn2 : p.dkl[o];
-    if (TEACHER) gb = p.dkl[o] * p.kl[o];
+    row_consts<TEACHER>(p.lse1[o], p.lse2[o], TEACHER ? p.kl[o] : 0.f, p.dkl[o], A1, A2);
   }
 
   f32x16 dq[NCB];
@@ -425,7 +460,7 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kerne
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             const int r = 8 * run + i;
-            ds[i] = dS_of<TEACHER>(s1[r], s2[r], c1, c2, L1, L2, ga, gb);
+            ds[i] = dS_abs<TEACHER>(s1[r], s2[r], c1, c2, A1, A2);
           }
           if (need_mask) {
 #pragma unroll
@@ -490,7 +525,7 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kerne
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t q = qw0 + acc_row(r, half);
-        if (q < p.NQ) dst[q * DG + 32 * cb + col] = dq[cb][r];
+        if (q < p.NQ) dst[q * DG + 32 * cb + col] = p.dkl[bh * p.NQ + q] < 0.f ? -dq[cb][r] : dq[cb][r];
       }
     return;
   }
@@ -500,8 +535,10 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kerne
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int64_t q = qw0 + acc_row(r, half);
-      if (q < p.NQ)
-        *reinterpret_cast<T*>(dqp + (q * p.sdq.n + 32 * cb + col) * ESZ) = from_f32<T>(dq[cb][r] * p.scale_g);
+      if (q < p.NQ) {
+        const float sc = p.dkl[bh * p.NQ + q] < 0.f ? -p.scale_g : p.scale_g;
+        *reinterpret_cast<T*>(dqp + (q * p.sdq.n + 32 * cb + col) * ESZ) = from_f32<T>(dq[cb][r] * sc);
+      }
     }
 }
 
