@@ -149,6 +149,9 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--mask", choices=["workload", "causal", "none"], default="workload",
+                    help="run the workload's shapes and inputs with causal masking or without "
+                         "(default: as the workload defines it)")
     ap.add_argument("--phases", default="fwd,student,teacher",
                     help="comma list of fwd, student, teacher, joint (profiling aid; the default is the "
                          "full step; --bwd-algo joint turns student,teacher into joint)")
@@ -182,6 +185,11 @@ def main(argv=None) -> int:
     skl.load()
 
     w = synth.WORKLOADS[args.workload]
+    traffic_key = w.name  # counter figures are recorded per workload as it is defined
+    if args.mask != "workload":
+        if w.causal != (args.mask == "causal"):
+            traffic_key = f"{w.name}_mask_{args.mask}"
+        w = w.with_(causal=args.mask == "causal")
     phases = [p for p in args.phases.split(",") if p]
     algo = args.bwd_algo
     if algo == "joint":
@@ -315,7 +323,7 @@ def main(argv=None) -> int:
             "peak": peak_tf,
             "unit": "TFLOP/s",
             "frac": ach / peak_tf,
-            "traffic": kernel_traffic(dom_name, dom_phase, w.name),
+            "traffic": kernel_traffic(dom_name, dom_phase, traffic_key),
             "flops_per_launch": dom_flops,
         },
         "cpu_baseline": None,
