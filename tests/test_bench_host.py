@@ -1,0 +1,43 @@
+"""Host-side logic of bench.py (no GPU): the one-GPU guard, the counter
+summary lookup and the flop model each kernel is measured against."""
+import os
+import subprocess
+import sys
+
+import bench
+from attention_kl_divergence_skl_amd import synth, workmodel
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_traffic_lookup_is_keyed_by_workload_phase_kernel_and_source():
+    with open(bench.TRAFFIC_FILE) as fh:
+        rows = [ln.split() for ln in fh if ln.startswith("traffic ")]
+    assert rows, "the counter summary holds data lines"
+    for f in rows:
+        assert len(f) == 6 and f[3] in bench.KERNEL_SOURCES and float(f[5]) > 0
+        wl, ph, k, sha = f[1:5]
+        got = bench.kernel_traffic(k, ph, wl)
+        # Reported only while the kernel sources hash to the recorded value.
+        assert got == (float(f[5]) if sha == bench.source_sha(k) else None)
+    # A workload run with another mask has no recorded figure.
+    assert bench.kernel_traffic("fwd_kernel", "fwd", "causal_64k_h32_d128_q1x4_mask_none") is None
+
+
+def test_kernel_flops_split_backward_recomputes_both_logits():
+    w = synth.WORKLOADS["causal_64k_h32_d128_q1x4"]
+    wk = workmodel.work(w.B, w.H, w.NQ, w.NK, w.d1, w.d2, w.causal, 2)
+    P = wk.pairs
+    assert bench.kernel_flops(w, wk, "fwd", "split") == {"fwd_kernel": wk.fwd_flops}
+    assert wk.fwd_flops == 2 * P * (w.d1 + w.d2)
+    st = bench.kernel_flops(w, wk, "student", "split")
+    assert st["bwd_dk_kernel"] == st["bwd_dq_kernel"] == 2 * P * (w.d1 + w.d2 + w.d2)
+    # The two split kernels together do more MFMA work than the algorithmic count.
+    assert sum(st.values()) > wk.student_flops
