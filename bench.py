@@ -13,7 +13,9 @@ Prints ONE JSON line.  `value` is the step's algorithmic TFLOP/s
 (2*pairs*[(d1+d2) + (d1+3*d2) + (3*d1+d2)] per step / step time).  The
 `roofline` object describes the kernel that takes the most time per step,
 timed with HIP events recorded by the library itself around that kernel on
-its launch stream; `cpu_baseline` is the float64 CPU oracle timed on a
+its launch stream: `achieved` is its share of the algorithmic flops (logits a
+split backward kernel recomputes count half) over its mean launch time, and
+`mfma_work_tflops` the rate of all the MFMA work it issues; `cpu_baseline` is the float64 CPU oracle timed on a
 bounded causal sub-problem of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
@@ -143,6 +145,24 @@ def kernel_flops(w, wk, phase: str, algo: str):
     return {"bwd_fused_kernel": wk.student_flops if phase == "student" else wk.teacher_flops}
 
 
+def kernel_alg_flops(w, wk, phase: str, algo: str):
+    """Algorithmic flops attributed to each main kernel of a phase: the
+    phase's algorithmic count (each pair's logits once, each gradient GEMM
+    once) shared out so that the kernels of a phase sum to it.  A kernel that
+    recomputes logits another kernel also forms is credited half of them."""
+    P = wk.pairs
+    if phase == "fwd":
+        return {"fwd_kernel": wk.fwd_flops}
+    if phase == "joint":
+        half = (wk.student_flops + wk.teacher_flops) // 2
+        return {"bwd_joint_dk_kernel": half, "bwd_joint_dq_kernel": half}
+    dg = w.d2 if phase == "student" else w.d1
+    if algo == "split":
+        per = P * (w.d1 + w.d2) + 2 * P * dg  # half of the logits + its own gradient GEMM
+        return {"bwd_dk_kernel": per, "bwd_dq_kernel": per}
+    return {"bwd_fused_kernel": wk.student_flops if phase == "student" else wk.teacher_flops}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -216,6 +236,7 @@ def main(argv=None) -> int:
 
     ws_s, ws_t = ws_for(False), ws_for(True)
     kflops = {p: kernel_flops(w, wk, p, algo) for p in phases}
+    kalg = {p: kernel_alg_flops(w, wk, p, algo) for p in phases}
     kev = {p: [] for p in phases}   # per call: events around its main kernels
     pev = {p: [] for p in phases}   # per call: events around the whole call
 
@@ -290,14 +311,19 @@ def main(argv=None) -> int:
         for i, (name, fl) in enumerate(kflops[p].items()):
             kms = float(np.mean([e[i].elapsed_time(e[i + 1]) for e in kev[p]]))
             tf = fl / (kms * 1e-3) / 1e12
-            ks[name] = {"ms": kms, "tflops": tf, "pct_mfma_peak": 100.0 * tf / peak_tf}
-            kernels.append((kms, p, name, fl))
+            atf = kalg[p][name] / (kms * 1e-3) / 1e12
+            # tflops / pct_mfma_peak: the kernel's own MFMA work (matrix-core use);
+            # alg_tflops / pct_peak_alg: its share of the algorithmic count.
+            ks[name] = {"ms": kms, "tflops": tf, "pct_mfma_peak": 100.0 * tf / peak_tf,
+                        "alg_tflops": atf, "pct_peak_alg": 100.0 * atf / peak_tf}
+            kernels.append((kms, p, name, kalg[p][name], fl))
         report[p] = {"call_ms": call_ms, "algorithmic_tflops": alg[p] / (call_ms * 1e-3) / 1e12,
                      "kernels": ks}
     step_flops = sum(alg[p] for p in phases)
     ms_step = elapsed / args.steps * 1e3
-    kms, dom_phase, dom_name, dom_flops = max(kernels)
+    kms, dom_phase, dom_name, dom_flops, dom_mfma = max(kernels)
     ach = dom_flops / (kms * 1e-3) / 1e12
+    mfma_rate = dom_mfma / (kms * 1e-3) / 1e12
     res = {
         "metric": METRIC,
         "value": step_flops / (ms_step * 1e-3) / 1e12,
@@ -325,6 +351,9 @@ def main(argv=None) -> int:
             "frac": ach / peak_tf,
             "traffic": kernel_traffic(dom_name, dom_phase, traffic_key),
             "flops_per_launch": dom_flops,
+            "mfma_work_flops_per_launch": dom_mfma,
+            "mfma_work_tflops": mfma_rate,
+            "mfma_work_frac": mfma_rate / peak_tf,
         },
         "cpu_baseline": None,
     }

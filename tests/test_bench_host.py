@@ -41,3 +41,19 @@ def test_kernel_flops_split_backward_recomputes_both_logits():
     assert st["bwd_dk_kernel"] == st["bwd_dq_kernel"] == 2 * P * (w.d1 + w.d2 + w.d2)
     # The two split kernels together do more MFMA work than the algorithmic count.
     assert sum(st.values()) > wk.student_flops
+
+
+def test_algorithmic_shares_sum_to_each_phase():
+    for name in ("causal_64k_h32_d128_q1x4", "causal_128k_h8_d128_d64"):
+        w = synth.WORKLOADS[name]
+        wk = workmodel.work(w.B, w.H, w.NQ, w.NK, w.d1, w.d2, w.causal, 2)
+        total = {"fwd": wk.fwd_flops, "student": wk.student_flops, "teacher": wk.teacher_flops}
+        for algo in ("split", "fused_atomic"):
+            for ph, t in total.items():
+                shares = bench.kernel_alg_flops(w, wk, ph, algo)
+                assert sum(shares.values()) == t
+                # never more than the kernel's own MFMA work
+                own = bench.kernel_flops(w, wk, ph, algo)
+                assert all(shares[k] <= own[k] for k in shares)
+        joint = bench.kernel_alg_flops(w, wk, "joint", "joint")
+        assert sum(joint.values()) == wk.student_flops + wk.teacher_flops
