@@ -156,31 +156,32 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dk_kerne
 
   // Query tiles go straight into a double-buffered LDS ring (loads of step
   // i+1 in flight during step i); the four per-row constants go through one
-  // register per thread.
-  float pv = 0.f;
+  // register per thread (wave w holds constant w of the tile's 64 rows).  The
+  // fetch only loads them: any arithmetic on a loaded value would make the
+  // wave wait for all its outstanding loads, the next tile's included, in the
+  // middle of the step, so the scaling happens at the stash after the step.
+  static_assert(4 * BQ == kThreads, "one wave per row constant");
+  const int which = tid / BQ, vrow = tid % BQ;  // which == wave
+  const float* const vsrc = which == 0 ? p.lse1 : which == 1 ? p.lse2 : p.dkl;
+  float pv = 0.f, pv2 = 0.f;
   auto fetch = [&](int st, int64_t q0) {
     tile_load_async<BQ, RB1>(sQ1[st], q1p, p.sq1.n * ESZ, (int)q0, (int)p.NQ, wave, lane);
     tile_load_async<BQ, RB2>(sQ2[st], q2p, p.sq2.n * ESZ, (int)q0, (int)p.NQ, wave, lane);
-    pv = 0.f;
-    if (tid < 4 * BQ) {
-      const int which = tid / BQ, row = tid % BQ;
-      const int64_t q = q0 + row;
-      if (q < p.NQ) {
-        const int64_t o = bh * p.NQ + q;
-        if (which == 0) pv = p.lse1[o] * kLog2e;
-        else if (which == 1) pv = p.lse2[o] * kLog2e;
-        else if (which == 2) pv = TEACHER ? p.dkl[o] * kLn2 : p.dkl[o];
-        else if (TEACHER) pv = p.dkl[o] * p.kl[o];
-      }
-    }
+    const int64_t q = q0 + vrow;
+    const int64_t o = bh * p.NQ + (q < p.NQ ? q : p.NQ - 1);  // rows past N_Q are zeroed at the stash
+    pv = vsrc[o];
+    if (TEACHER && which == 3) pv2 = p.kl[o];
   };
-  auto stash = [&](int st) {
-    if (tid < 4 * BQ) sVec[st][tid / BQ][tid % BQ] = pv;
+  auto stash = [&](int st, int64_t q0) {
+    float v;
+    if (which == 3) v = TEACHER ? pv * pv2 : 0.f;                 // g KL (teacher)
+    else v = pv * (which == 2 ? (TEACHER ? kLn2 : 1.f) : kLog2e);  // L1, L2 (base 2), ga
+    sVec[st][which][vrow] = (q0 + vrow < p.NQ) ? v : 0.f;
   };
 
   if (nsteps > 0) {
     fetch(0, qbeg);
-    stash(0);
+    stash(0, qbeg);
   }
   wait_vm();
   __syncthreads();
@@ -215,30 +216,22 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dk_kerne
       // The two chains alternate, so each MFMA's predecessor in its chain is
       // two issues back.
       const int qrow = 32 * qb + prow;
-      if constexpr (TEACHER) {
-        // Teacher: the operands of chunk c + 1 are read while chunk c's
-        // MFMAs issue, the order pinned by a scheduling barrier (-1.5%; the
-        // student kernel, with less register room, ran 0.6% slower so).
-        constexpr int NCM = NC1 > NC2 ? NC1 : NC2;
-        frag pa1[2], pa2[2];
-        auto ld = [&](int c, int slot) __attribute__((always_inline)) {
-          if (c < NC1) pa1[slot] = M::load(&sQ1[st][T1::off(qrow, (c * KC + half * EPL) * ESZ)]);
-          if (c < NC2) pa2[slot] = M::load(&sQ2[st][T2::off(qrow, (c * KC + half * EPL) * ESZ)]);
-        };
-        ld(0, 0);
+      // The operands of chunk c + 1 are read while chunk c's MFMAs issue,
+      // the order pinned by a scheduling barrier (the compiler otherwise
+      // issues each pair of reads just before its MFMAs and waits on them).
+      constexpr int NCM = NC1 > NC2 ? NC1 : NC2;
+      frag pa1[2], pa2[2];
+      auto ld = [&](int c, int slot) __attribute__((always_inline)) {
+        if (c < NC1) pa1[slot] = M::load(&sQ1[st][T1::off(qrow, (c * KC + half * EPL) * ESZ)]);
+        if (c < NC2) pa2[slot] = M::load(&sQ2[st][T2::off(qrow, (c * KC + half * EPL) * ESZ)]);
+      };
+      ld(0, 0);
 #pragma unroll
-        for (int c = 0; c < NCM; ++c) {
-          if (c + 1 < NCM) ld(c + 1, (c + 1) & 1);
-          __builtin_amdgcn_sched_barrier(0);
-          if (c < NC1) s1 = M::run(pa1[c & 1], kf1[c], s1);
-          if (c < NC2) s2 = M::run(pa2[c & 1], kf2[c], s2);
-        }
-      } else {
-#pragma unroll
-        for (int c = 0; c < (NC1 > NC2 ? NC1 : NC2); ++c) {
-          if (c < NC1) s1 = M::run(M::load(&sQ1[st][T1::off(qrow, (c * KC + half * EPL) * ESZ)]), kf1[c], s1);
-          if (c < NC2) s2 = M::run(M::load(&sQ2[st][T2::off(qrow, (c * KC + half * EPL) * ESZ)]), kf2[c], s2);
-        }
+      for (int c = 0; c < NCM; ++c) {
+        if (c + 1 < NCM) ld(c + 1, (c + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (c < NC1) s1 = M::run(pa1[c & 1], kf1[c], s1);
+        if (c < NC2) s2 = M::run(pa2[c & 1], kf2[c], s2);
       }
 
       __builtin_amdgcn_s_setprio(0);
@@ -304,7 +297,7 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dk_kerne
         }
       }
     }
-    if (it + 1 < nsteps) stash(st ^ 1);
+    if (it + 1 < nsteps) stash(st ^ 1, q0 + BQ);
     wait_vm();
     __syncthreads();
   };
