@@ -107,30 +107,31 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_joint_dk_kernel(const BwdPara
   if (CAUSAL) qbeg = max((int64_t)0, kt0 - off) / BQ * BQ;
   const int64_t nsteps = (p.NQ - qbeg + BQ - 1) / BQ;
 
-  float pv = 0.f;
+  // Row constants of the next query tile (wave w holds constant w of its 64
+  // rows): the fetch only loads them and the stash, after the step's
+  // compute, scales them, so no wave waits for the next tile's loads
+  // mid-step (any arithmetic on a loaded value makes it wait for all of its
+  // outstanding loads).
+  static_assert(4 * BQ == kThreads, "one wave per row constant");
+  const int which = tid / BQ, vrow = tid % BQ;  // which == wave
+  const float* const vsrc = which == 0 ? p.lse1 : which == 1 ? p.lse2 : p.dkl;
+  float pv = 0.f, pv2 = 0.f;
   auto fetch = [&](int st, int64_t q0) {
     tile_load_async<BQ, RB1>(sQ1[st], q1p, p.sq1.n * ESZ, (int)q0, (int)p.NQ, wave, lane);
     tile_load_async<BQ, RB2>(sQ2[st], q2p, p.sq2.n * ESZ, (int)q0, (int)p.NQ, wave, lane);
-    pv = 0.f;
-    if (tid < 4 * BQ) {
-      const int which = tid / BQ, row = tid % BQ;
-      const int64_t q = q0 + row;
-      if (q < p.NQ) {
-        const int64_t o = bh * p.NQ + q;
-        if (which == 0) pv = p.lse1[o] * kLog2e;
-        else if (which == 1) pv = p.lse2[o] * kLog2e;
-        else if (which == 2) pv = p.dkl[o];
-        else pv = p.dkl[o] * p.kl[o];
-      }
-    }
+    const int64_t q = q0 + vrow;
+    const int64_t o = bh * p.NQ + (q < p.NQ ? q : p.NQ - 1);  // rows past N_Q are zeroed at the stash
+    pv = vsrc[o];
+    if (which == 3) pv2 = p.kl[o];
   };
-  auto stash = [&](int st) {
-    if (tid < 4 * BQ) sVec[st][tid / BQ][tid % BQ] = pv;
+  auto stash = [&](int st, int64_t q0) {
+    const float v = which == 3 ? pv * pv2 : which == 2 ? pv : pv * kLog2e;  // L1, L2 (base 2), g, g KL
+    sVec[st][which][vrow] = (q0 + vrow < p.NQ) ? v : 0.f;
   };
 
   if (nsteps > 0) {
     fetch(0, qbeg);
-    stash(0);
+    stash(0, qbeg);
   }
   wait_vm();
   __syncthreads();
@@ -226,7 +227,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_joint_dk_kernel(const BwdPara
         }
       }
     }
-    if (it + 1 < nsteps) stash(st ^ 1);
+    if (it + 1 < nsteps) stash(st ^ 1, q0 + BQ);
     wait_vm();
     __syncthreads();
   };
