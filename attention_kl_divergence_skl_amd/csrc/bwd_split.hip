@@ -365,8 +365,13 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kerne
   using T2 = SwzTile<RB2>;
   using TG = SwzTile<RBG>;
 
-  __shared__ __attribute__((aligned(1024))) char sK1[2][BK * RB1];
-  __shared__ __attribute__((aligned(1024))) char sK2[2][BK * RB2];
+  // Ring stages as separate LDS variables, so that the compiler can tell
+  // reads of one stage from the direct-to-LDS loads in flight into the other
+  // and does not wait for those loads before them.
+  __shared__ __attribute__((aligned(1024))) char sK1a[BK * RB1], sK1b[BK * RB1];
+  __shared__ __attribute__((aligned(1024))) char sK2a[BK * RB2], sK2b[BK * RB2];
+  auto sK1 = [&](int st) __attribute__((always_inline)) -> char* { return st ? sK1b : sK1a; };
+  auto sK2 = [&](int st) __attribute__((always_inline)) -> char* { return st ? sK2b : sK2a; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -427,8 +432,8 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kerne
   const int wave_kmax = CAUSAL ? qw0 + 31 + off : NK - 1;
 
   auto fetch = [&](int st, int j0) {
-    tile_load_async<BK, RB1>(sK1[st], k1p, p.sk1.n * ESZ, j0, NK, wave, lane);
-    tile_load_async<BK, RB2>(sK2[st], k2p, p.sk2.n * ESZ, j0, NK, wave, lane);
+    tile_load_async<BK, RB1>(sK1(st), k1p, p.sk1.n * ESZ, j0, NK, wave, lane);
+    tile_load_async<BK, RB2>(sK2(st), k2p, p.sk2.n * ESZ, j0, NK, wave, lane);
   };
 
   if (nsteps > 0) fetch(0, kbeg);
@@ -450,7 +455,7 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kerne
       // (Here the per-chunk LDS offsets are left to the compiler, which keeps
       // them as loop invariants: measured faster than forming them at each
       // read as the dK kernel does.)
-      const char* kg = TEACHER ? &sK1[st][0] : &sK2[st][0];
+      const char* kg = TEACHER ? sK1(st) : sK2(st);
 #pragma unroll
       for (int kb = 0; kb < BK / 32; ++kb) {
         f32x16 s1 = f32x16{}, s2 = f32x16{};
@@ -460,8 +465,8 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dq_kerne
         const int krow = kb * 32 + prow;
 #pragma unroll
         for (int c = 0; c < (NC1 > NC2 ? NC1 : NC2); ++c) {  // chains alternate (see the dK kernel)
-          if (c < NC1) s1 = M::run(M::load(&sK1[st][T1::off(krow, (c * KC + half * EPL) * ESZ)]), qf1[c], s1);
-          if (c < NC2) s2 = M::run(M::load(&sK2[st][T2::off(krow, (c * KC + half * EPL) * ESZ)]), qf2[c], s2);
+          if (c < NC1) s1 = M::run(M::load(&sK1(st)[T1::off(krow, (c * KC + half * EPL) * ESZ)]), qf1[c], s1);
+          if (c < NC2) s2 = M::run(M::load(&sK2(st)[T2::off(krow, (c * KC + half * EPL) * ESZ)]), qf2[c], s2);
         }
         __builtin_amdgcn_s_setprio(0);
         // Registers 8 run .. 8 run + 7 hold keys kb 32 + 16 run + 8 half + 0..7:

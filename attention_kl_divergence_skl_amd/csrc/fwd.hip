@@ -54,8 +54,13 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(c
   constexpr int RB1 = D1 * ESZ, RB2 = D2 * ESZ;  // bytes per key row
   using T1 = SwzTile<RB1>;
   using T2 = SwzTile<RB2>;
-  __shared__ __attribute__((aligned(1024))) char sK1[2][BK * RB1];
-  __shared__ __attribute__((aligned(1024))) char sK2[2][BK * RB2];
+  // The two stages of the ring are separate LDS variables: the compiler can
+  // then tell that reads of one stage do not alias the direct-to-LDS loads in
+  // flight into the other, and does not wait for those loads before them.
+  __shared__ __attribute__((aligned(1024))) char sK1a[BK * RB1], sK1b[BK * RB1];
+  __shared__ __attribute__((aligned(1024))) char sK2a[BK * RB2], sK2b[BK * RB2];
+  auto sK1 = [&](int st) __attribute__((always_inline)) -> char* { return st ? sK1b : sK1a; };
+  auto sK2 = [&](int st) __attribute__((always_inline)) -> char* { return st ? sK2b : sK2a; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -113,8 +118,8 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(c
   // of tile i+1 are in flight while tile i is computed; one barrier per tile.
   const int64_t rs1 = p.sk1.n * ESZ, rs2 = p.sk2.n * ESZ;
   auto fetch = [&](int st, int j0) {
-    tile_load_async<BK, RB1>(sK1[st], k1p, rs1, j0, NK, wave, lane);
-    tile_load_async<BK, RB2>(sK2[st], k2p, rs2, j0, NK, wave, lane);
+    tile_load_async<BK, RB1>(sK1(st), k1p, rs1, j0, NK, wave, lane);
+    tile_load_async<BK, RB2>(sK2(st), k2p, rs2, j0, NK, wave, lane);
   };
 
   const float c1 = p.c1, c2 = p.c2;
@@ -143,9 +148,9 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(c
     constexpr int st = decltype(stc)::value;
     frag ka1[NC1], ka2[NC2];
 #pragma unroll
-    for (int c = 0; c < NC1; ++c) ka1[c] = M::load(&sK1[st][kb * 32 * RB1 + aoff1[c]]);
+    for (int c = 0; c < NC1; ++c) ka1[c] = M::load(&sK1(st)[kb * 32 * RB1 + aoff1[c]]);
 #pragma unroll
-    for (int c = 0; c < NC2; ++c) ka2[c] = M::load(&sK2[st][kb * 32 * RB2 + aoff2[c]]);
+    for (int c = 0; c < NC2; ++c) ka2[c] = M::load(&sK2(st)[kb * 32 * RB2 + aoff2[c]]);
     s1 = f32x16{};
     s2 = f32x16{};
     // Raised wave priority while the MFMAs issue: the other wave of the SIMD,
