@@ -109,3 +109,73 @@ def test_backward_mutants_are_caught(monkeypatch, mutant):
 def test_unmutated_oracle_passes_the_same_pins():
     _run_forward_pins()
     _run_backward_pins()
+
+
+# ------------------------------------------ mutants of the batched wrappers ----
+
+import oracle  # noqa: E402  (the package re-exports forward/backward by name)
+
+_orig_forward = orc.forward
+_orig_backward = orc.backward
+
+
+def _fwd_swapped_scales(q1, k1, q2, k2, scale1, scale2, causal):
+    return _orig_forward(q1, k1, q2, k2, scale2, scale1, causal)
+
+
+def _fwd_wrong_head(q1, k1, q2, k2, scale1, scale2, causal):
+    """K2 taken from the next head (a plausible indexing slip in the loop)."""
+    out = _orig_forward(q1, k1, q2, k2, scale1, scale2, causal)
+    H = q1.shape[1]
+    for b in range(q1.shape[0]):
+        for h in range(H):
+            r = orc.head_forward(q1[b, h], k1[b, h], q2[b, h], k2[b, (h + 1) % H], scale1, scale2, causal)
+            for k in out:
+                out[k][b, h] = r[k]
+    return out
+
+
+def _bwd_wrong_head_g(q1, k1, q2, k2, scale1, scale2, causal, g, setting):
+    return _orig_backward(q1, k1, q2, k2, scale1, scale2, causal, g[:, ::-1].copy(), setting)
+
+
+def _bwd_swapped_scales(q1, k1, q2, k2, scale1, scale2, causal, g, setting):
+    return _orig_backward(q1, k1, q2, k2, scale2, scale1, causal, g, setting)
+
+
+def _bwd_wrong_head_out(q1, k1, q2, k2, scale1, scale2, causal, g, setting):
+    """dK of head h stored into head h + 1."""
+    dq, dk = _orig_backward(q1, k1, q2, k2, scale1, scale2, causal, g, setting)
+    return dq, np.roll(dk, 1, axis=1)
+
+
+def _run_batched_forward_pins():
+    for causal in (False, True):
+        pins.test_batched_forward_matches_brute_force_per_head(causal)
+
+
+def _run_batched_backward_pins():
+    for setting in ("student", "teacher"):
+        for causal in (False, True):
+            pins.test_batched_backward_matches_finite_differences(setting, causal)
+
+
+@pytest.mark.parametrize("mutant", [_fwd_swapped_scales, _fwd_wrong_head])
+def test_batched_forward_mutants_are_caught(monkeypatch, mutant):
+    monkeypatch.setattr(orc, "forward", mutant)
+    monkeypatch.setattr(oracle, "forward", mutant)
+    with pytest.raises(AssertionError):
+        _run_batched_forward_pins()
+
+
+@pytest.mark.parametrize("mutant", [_bwd_wrong_head_g, _bwd_swapped_scales, _bwd_wrong_head_out])
+def test_batched_backward_mutants_are_caught(monkeypatch, mutant):
+    monkeypatch.setattr(orc, "backward", mutant)
+    monkeypatch.setattr(oracle, "backward", mutant)
+    with pytest.raises(AssertionError):
+        _run_batched_backward_pins()
+
+
+def test_unmutated_batched_wrappers_pass_the_same_pins():
+    _run_batched_forward_pins()
+    _run_batched_backward_pins()

@@ -289,3 +289,85 @@ def test_teacher_gradient_is_finite_when_probabilities_underflow():
         for setting in ("student", "teacher"):
             dq, dk = oracle.head_backward(q1, k1, q2, k2, 1.0, 1.0, causal, g, setting)
             assert np.all(np.isfinite(dq)) and np.all(np.isfinite(dk))
+
+
+# ------------------------------------------------ batched [B, H, N, d] calls ----
+#
+# oracle.forward / oracle.backward loop over (batch, head) and call the
+# per-head functions.  These pins check the loop itself: every (b, h) slice of
+# the output must come from the same (b, h) slices of all four inputs (and of
+# g), with scale1 on the (Q1, K1) side and scale2 on the (Q2, K2) side.  The
+# shapes make every axis distinguishable: B != H, N_Q != N_K, d1 != d2 and
+# unequal scales.
+
+BATCHED_SHAPE = dict(B=2, H=3, nq=5, nk=7, d1=3, d2=2)
+BATCHED_SCALES = (0.9, 0.35)
+
+
+def _batched_inputs(seed):
+    s = BATCHED_SHAPE
+    rng = np.random.default_rng(seed)
+    q1 = 1.5 * rng.standard_normal((s["B"], s["H"], s["nq"], s["d1"]))
+    k1 = rng.standard_normal((s["B"], s["H"], s["nk"], s["d1"]))
+    q2 = rng.standard_normal((s["B"], s["H"], s["nq"], s["d2"]))
+    k2 = rng.standard_normal((s["B"], s["H"], s["nk"], s["d2"]))
+    g = rng.standard_normal((s["B"], s["H"], s["nq"]))
+    return q1, k1, q2, k2, g
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_batched_forward_matches_brute_force_per_head(causal):
+    q1, k1, q2, k2, _ = _batched_inputs(41)
+    sc1, sc2 = BATCHED_SCALES
+    r = oracle.forward(q1, k1, q2, k2, sc1, sc2, causal)
+    B, H = q1.shape[:2]
+    for k in ("kl", "lse1", "lse2"):
+        assert r[k].shape == (B, H, q1.shape[2])
+    for b in range(B):
+        for h in range(H):
+            kl, lse1, lse2 = _brute(q1[b, h], k1[b, h], q2[b, h], k2[b, h], sc1, sc2, causal)
+            np.testing.assert_allclose(r["kl"][b, h], kl, rtol=1e-10, atol=1e-13)
+            np.testing.assert_allclose(r["lse1"][b, h], lse1, rtol=1e-12)
+            np.testing.assert_allclose(r["lse2"][b, h], lse2, rtol=1e-12)
+
+
+def _batched_brute_loss(q1, k1, q2, k2, sc1, sc2, causal, g):
+    """sum over (b, h, i) of g[b, h, i] * KL[b, h, i], all in scalar Python."""
+    total = 0.0
+    for b in range(q1.shape[0]):
+        for h in range(q1.shape[1]):
+            kl, _, _ = _brute(q1[b, h], k1[b, h], q2[b, h], k2[b, h], sc1, sc2, causal)
+            total += float(np.dot(g[b, h], kl))
+    return total
+
+
+@pytest.mark.parametrize("setting", ["student", "teacher"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_batched_backward_matches_finite_differences(setting, causal):
+    """Central differences of the scalar brute-force loss with respect to
+    every element of every head: a gradient written to the wrong head, or
+    computed from another head's inputs or g, fails here."""
+    q1, k1, q2, k2, g = _batched_inputs(42)
+    sc1, sc2 = BATCHED_SCALES
+    dq, dk = oracle.backward(q1, k1, q2, k2, sc1, sc2, causal, g, setting)
+    args = [q1, k1, q2, k2]
+    iq, ik = (2, 3) if setting == "student" else (0, 1)
+    assert dq.shape == args[iq].shape and dk.shape == args[ik].shape
+    for idx, analytic in ((iq, dq), (ik, dk)):
+        num = np.zeros_like(args[idx])
+        for pos in np.ndindex(*args[idx].shape):
+            x0 = args[idx][pos]
+            h = 1e-6 * max(1.0, abs(x0))
+            a = [x.copy() for x in args]
+            a[idx][pos] = x0 + h
+            fp = _batched_brute_loss(*a, sc1, sc2, causal, g)
+            a[idx][pos] = x0 - h
+            fm = _batched_brute_loss(*a, sc1, sc2, causal, g)
+            num[pos] = (fp - fm) / (2 * h)
+        err = np.linalg.norm(analytic - num) / max(np.linalg.norm(num), 1e-30)
+        assert err <= 1e-6, f"{setting} input {idx}: relative error {err:.3e}"
+        # Per head as well, so that one head's error cannot hide in the total.
+        for b in range(num.shape[0]):
+            for hh in range(num.shape[1]):
+                eh = np.linalg.norm(analytic[b, hh] - num[b, hh])
+                assert eh <= 1e-6 * max(np.linalg.norm(num[b, hh]), 1e-4), (setting, idx, b, hh, eh)
