@@ -254,6 +254,27 @@ def skl_backward_workspace_size(q1, k1, q2, k2, teacher: bool, algo="split") -> 
     return int(load().skl_backward_workspace_size(ctypes.byref(s), int(bool(teacher)), _algo(algo)))
 
 
+def _disjoint_layout(strides, B, H, N, d) -> bool:
+    """Host check of the library's rule for gradient layouts: taking the
+    (b, h, n) axes of size > 1 in order of increasing stride, each stride must
+    reach past the span of the axes inside it (the d axis spans d elements)."""
+    span = d
+    for size, st in sorted(zip((B, H, N), strides), key=lambda a: a[1]):
+        if size <= 1:
+            continue
+        if st < span:
+            return False
+        span += st * (size - 1)
+    return True
+
+
+def _own_layout(t):
+    """t itself if every element has its own address, else a contiguous copy
+    (e.g. a K broadcast over heads with expand())."""
+    B, H, N, d = t.shape
+    return t if _disjoint_layout(_bhn_strides(t), B, H, N, d) else t.contiguous()
+
+
 def _grad_like(t):
     import torch
 
@@ -366,6 +387,10 @@ def _autograd_function():
             q1, k1, q2, k2, kl, lse1, lse2 = ctx.saved_tensors
             scale1, scale2, causal, algo = ctx.args
             g = g.float().contiguous()
+            # Gradients take their input's strides; an input that repeats
+            # elements (broadcast over heads or batches) is copied first, and
+            # autograd sums the copy's gradient back over the broadcast axes.
+            q1, k1, q2, k2 = (_own_layout(x) for x in (q1, k1, q2, k2))
             dq1 = dk1 = dq2 = dk2 = None
             need_s = ctx.needs_input_grad[2] or ctx.needs_input_grad[3]
             need_t = ctx.needs_input_grad[0] or ctx.needs_input_grad[1]

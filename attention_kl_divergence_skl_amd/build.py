@@ -33,9 +33,10 @@ HIPCC_FLAGS = [
 # Per-source additions.  The forward's running max is an fmaxf tree over MFMA
 # results; under IEEE NaN semantics every operand is first quieted with an
 # extra v_max_f32 (one VALU op per logit, about a sixth of the kernel's VALU
-# work).  The forward never produces a NaN that it consumes (masked logits are
-# -inf and are selected away before any inf - inf is used; an all-masked row
-# works with m = 0), so it is compiled without NaN semantics.
+# work).  The forward never produces a NaN that it consumes: masked logits are
+# -inf and are selected away before any inf - inf is used, and the running
+# maxima start at the finite kNoKey = -1e30 (so a lane whose keys are all
+# masked keeps finite shifts); it is therefore compiled without NaN semantics.
 SOURCE_FLAGS = {"fwd.hip": ["-fno-honor-nans"]}
 
 

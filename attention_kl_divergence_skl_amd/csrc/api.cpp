@@ -104,6 +104,50 @@ skl_status check_ptr(const void* p, const char* name, bool align16 = true) {
   return ok();
 }
 
+// A 1-D dispatch holds at most 2^32 - 1 work-items, i.e. this many
+// 256-thread workgroups.  Every launch with one workgroup per tile checks its
+// grid against it on the host (the fill, convert and reduce kernels loop over
+// their elements and cap their grids).
+constexpr int64_t kMaxWorkgroups = ((int64_t(1) << 32) - 1) / skl::kThreads;
+
+skl_status check_grid(int64_t groups, const char* what) {
+  if (groups > kMaxWorkgroups)
+    return fail(SKL_ERR_UNSUPPORTED, "%s: %lld workgroups exceed the dispatch limit of %lld", what,
+                (long long)groups, (long long)kMaxWorkgroups);
+  return ok();
+}
+
+// True when the [B, H, N, d] view with (b, h, n) element strides `st` and a
+// contiguous d axis gives every element its own address: taking the axes of
+// size > 1 in order of increasing stride, each stride reaches past everything
+// the axes inside it span.  (Sufficient, not necessary: exotic interleaved
+// layouts that happen to be one-to-one are rejected too.)
+bool disjoint_layout(const int64_t st[3], int64_t B, int64_t H, int64_t N, int64_t d) {
+  int64_t size[3] = {B, H, N}, stride[3] = {st[0], st[1], st[2]};
+  int idx[3] = {0, 1, 2};
+  std::sort(idx, idx + 3, [&](int a, int b) { return stride[a] < stride[b]; });
+  int64_t span = d;  // offsets [0, span) are covered by the axes inside
+  for (int k = 0; k < 3; ++k) {
+    const int a = idx[k];
+    if (size[a] <= 1) continue;
+    if (stride[a] < span) return false;
+    span += stride[a] * (size[a] - 1);
+  }
+  return true;
+}
+
+// Gradients are written with the strides of the corresponding input, so an
+// input whose layout repeats elements (a stride of 0, e.g. one K broadcast
+// over heads, or overlapping rows) cannot receive its gradient in place.
+skl_status check_grad_layout(const int64_t st[3], int64_t B, int64_t H, int64_t N, int64_t d, const char* name) {
+  if (!disjoint_layout(st, B, H, N, d))
+    return fail(SKL_ERR_UNSUPPORTED,
+                "%s: the gradient takes this input's strides, which map several elements to one address "
+                "(a zero or overlapping stride); pass a copy with a one-to-one layout",
+                name);
+  return ok();
+}
+
 skl_status check_scales(float s1, float s2, int causal, const skl_shape* s) {
   if (!std::isfinite(s1) || !std::isfinite(s2) || !(s1 > 0.f) || !(s2 > 0.f))
     return fail(SKL_ERR_INVALID_ARGUMENT, "scales must be finite and > 0 (got %g, %g)", (double)s1, (double)s2);
@@ -194,6 +238,7 @@ skl_status skl_forward(const skl_shape* s, const void* q1, const void* k1, const
   SKL_TRY(check_ptr(kl, "kl", false));
   SKL_TRY(check_ptr(lse1, "lse1", false));
   SKL_TRY(check_ptr(lse2, "lse2", false));
+  SKL_TRY(check_grid(s->B * s->H * cdiv(s->NQ, skl::kFwdBQ), "skl_forward"));
   skl::FwdParams p = fwd_params(s, q1, k1, q2, k2, scale1, scale2);
   p.kl = kl;
   p.lse1 = lse1;
@@ -219,8 +264,7 @@ skl_status skl_forward_splitk(const skl_shape* s, const void* q1, const void* k1
   const size_t need = skl_forward_splitk_workspace_size(s, num_splits);
   if (ws_bytes < need)
     return fail(SKL_ERR_WORKSPACE_TOO_SMALL, "split-K workspace %zu < %zu bytes", ws_bytes, need);
-  if ((int64_t)s->B * s->H * cdiv(s->NQ, skl::kFwdBQ) * num_splits > (int64_t(1) << 31) - 1)
-    return fail(SKL_ERR_UNSUPPORTED, "grid too large");
+  SKL_TRY(check_grid(s->B * s->H * cdiv(s->NQ, skl::kFwdBQ) * num_splits, "skl_forward_splitk"));
   skl::FwdParams p = fwd_params(s, q1, k1, q2, k2, scale1, scale2);
   p.splits = num_splits;
   p.split_len = (int32_t)split_len_for(s->NK, num_splits);
@@ -322,6 +366,12 @@ static skl_status backward_common(const skl_shape* s, const void* q1, const void
   if (algo != SKL_BWD_SPLIT && algo != SKL_BWD_FUSED_ATOMIC)
     return fail(SKL_ERR_INVALID_ARGUMENT, "unknown backward algorithm %d", algo);
   const bool fused = algo == SKL_BWD_FUSED_ATOMIC;
+  const int64_t* sqg = teacher ? s->sq1 : s->sq2;
+  const int64_t* skg = teacher ? s->sk1 : s->sk2;
+  const int64_t dgd = teacher ? s->d1 : s->d2;
+  SKL_TRY(check_grad_layout(sqg, s->B, s->H, s->NQ, dgd, teacher ? "q1" : "q2"));
+  SKL_TRY(check_grad_layout(skg, s->B, s->H, s->NK, dgd, teacher ? "k1" : "k2"));
+  SKL_TRY(check_grid(s->B * s->H * cdiv(s->NK, skl::kBwdBK), "backward (key tiles)"));
   if (fused) {
     SKL_TRY(check_ptr(ws, "ws"));
     const size_t need = skl_backward_workspace_size(s, teacher ? 1 : 0, algo);
@@ -377,6 +427,7 @@ static skl_status backward_common(const skl_shape* s, const void* q1, const void
     const int64_t splits = dq_splits_for(s);
     const size_t need = skl_backward_workspace_size(s, teacher ? 1 : 0, algo);
     const bool split_dq = splits > 1 && ws != nullptr && ws_bytes >= need;
+    SKL_TRY(check_grid(BH * cdiv(s->NQ, 128) * (split_dq ? splits : 1), "backward (query tiles)"));
     if (split_dq) {
       if (reinterpret_cast<uintptr_t>(ws) % 16 != 0) return fail(SKL_ERR_UNSUPPORTED, "ws must be 16-byte aligned");
       p.dq_splits = (int32_t)splits;
@@ -443,6 +494,10 @@ skl_status skl_backward_joint(const skl_shape* s, const void* q1, const void* k1
   SKL_TRY(check_ptr(dk1, "dk1"));
   SKL_TRY(check_ptr(dq2, "dq2"));
   SKL_TRY(check_ptr(dk2, "dk2"));
+  SKL_TRY(check_grad_layout(s->sq1, s->B, s->H, s->NQ, s->d1, "q1"));
+  SKL_TRY(check_grad_layout(s->sk1, s->B, s->H, s->NK, s->d1, "k1"));
+  SKL_TRY(check_grad_layout(s->sq2, s->B, s->H, s->NQ, s->d2, "q2"));
+  SKL_TRY(check_grad_layout(s->sk2, s->B, s->H, s->NK, s->d2, "k2"));
 
   const size_t need_s = skl_backward_workspace_size(s, 0, SKL_BWD_SPLIT);
   const size_t need_t = skl_backward_workspace_size(s, 1, SKL_BWD_SPLIT);
@@ -457,6 +512,8 @@ skl_status skl_backward_joint(const skl_shape* s, const void* q1, const void* k1
   }
 
   const int64_t BH = s->B * s->H;
+  SKL_TRY(check_grid(BH * cdiv(s->NK, skl::kBwdBK), "joint backward (key tiles)"));
+  SKL_TRY(check_grid(BH * cdiv(s->NQ, 128), "joint backward (query tiles)"));
   skl::BwdParams p{};
   p.q1 = q1;
   p.k1 = k1;

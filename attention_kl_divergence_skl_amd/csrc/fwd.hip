@@ -313,32 +313,34 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(c
   }
 }
 
-// Merge split-K partials: one thread per row.
+// Merge split-K partials: one thread per row (grid-stride, so any row count
+// fits one launch).
 __global__ __launch_bounds__(256) void reduce_kernel(const ReduceParams p) {
-  const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (row >= p.rows) return;
-  const int64_t bh = row / p.NQ, i = row % p.NQ;
-  const int64_t stride_f = p.rows * p.splits;
-  const float* src = p.part + bh * p.splits * p.NQ + i;
-  float M1 = neg_inf(), M2 = neg_inf();
-  for (int s = 0; s < p.splits; ++s) {
-    M1 = fmaxf(M1, src[s * p.NQ]);
-    M2 = fmaxf(M2, src[2 * stride_f + s * p.NQ]);
+  for (int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; row < p.rows;
+       row += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t bh = row / p.NQ, i = row % p.NQ;
+    const int64_t stride_f = p.rows * p.splits;
+    const float* src = p.part + bh * p.splits * p.NQ + i;
+    float M1 = neg_inf(), M2 = neg_inf();
+    for (int s = 0; s < p.splits; ++s) {
+      M1 = fmaxf(M1, src[s * p.NQ]);
+      M2 = fmaxf(M2, src[2 * stride_f + s * p.NQ]);
+    }
+    const float M1u = (M1 == neg_inf()) ? 0.f : M1;
+    const float M2u = (M2 == neg_inf()) ? 0.f : M2;
+    float L1 = 0.f, L2 = 0.f, ACC = 0.f;
+    for (int s = 0; s < p.splits; ++s) {
+      const float w1 = exp2_hw(src[s * p.NQ] - M1u);
+      const float w2 = exp2_hw(src[2 * stride_f + s * p.NQ] - M2u);
+      L1 = fmaf(src[stride_f + s * p.NQ], w1, L1);
+      ACC = fmaf(src[4 * stride_f + s * p.NQ], w1, ACC);
+      L2 = fmaf(src[3 * stride_f + s * p.NQ], w2, L2);
+    }
+    const float lg1 = log2f(L1), lg2 = log2f(L2);
+    p.lse1[row] = kLn2 * (M1 + lg1);
+    p.lse2[row] = kLn2 * (M2 + lg2);
+    p.kl[row] = kLn2 * (ACC / L1 + (M2 - M1) + (lg2 - lg1));
   }
-  const float M1u = (M1 == neg_inf()) ? 0.f : M1;
-  const float M2u = (M2 == neg_inf()) ? 0.f : M2;
-  float L1 = 0.f, L2 = 0.f, ACC = 0.f;
-  for (int s = 0; s < p.splits; ++s) {
-    const float w1 = exp2_hw(src[s * p.NQ] - M1u);
-    const float w2 = exp2_hw(src[2 * stride_f + s * p.NQ] - M2u);
-    L1 = fmaf(src[stride_f + s * p.NQ], w1, L1);
-    ACC = fmaf(src[4 * stride_f + s * p.NQ], w1, ACC);
-    L2 = fmaf(src[3 * stride_f + s * p.NQ], w2, L2);
-  }
-  const float lg1 = log2f(L1), lg2 = log2f(L2);
-  p.lse1[row] = kLn2 * (M1 + lg1);
-  p.lse2[row] = kLn2 * (M2 + lg2);
-  p.kl[row] = kLn2 * (ACC / L1 + (M2 - M1) + (lg2 - lg1));
 }
 
 namespace {
@@ -374,7 +376,8 @@ hipError_t launch_forward(const FwdParams& p, int dtype, int d1, int d2, bool ca
 }
 
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s) {
-  const int64_t blocks = (p.rows + 255) / 256;
+  int64_t blocks = (p.rows + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
   hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
   return hipGetLastError();
 }

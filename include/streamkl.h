@@ -27,8 +27,9 @@
  * - Causal masking is bottom-right aligned: row i sees keys
  *   j <= i + (N_K - N_Q); causal calls need N_Q <= N_K.
  * - All pointers except skl_shape are DEVICE pointers owned by the caller.
- *   The library never allocates or frees device memory and keeps no state
- *   between calls except a thread-local error message (skl_last_error).
+ *   The library never allocates or frees device memory.  Between calls it
+ *   keeps only thread-local host state: the last error message
+ *   (skl_last_error) and the profiling events of skl_set_kernel_events.
  * - Every call only enqueues work on `stream` and returns; it never
  *   synchronises.  Calls on one stream run in order.
  * - Validation happens on the host before anything is enqueued; on any
@@ -38,6 +39,17 @@
  *   N_Q > 0 is invalid (an empty softmax).
  * - N_Q and N_K must be below 2^30 and B * H at most 2^31 (row indices are
  *   32-bit inside the kernels); larger sizes return SKL_ERR_UNSUPPORTED.
+ *   So does a shape whose kernels would need more than (2^32 - 1) / 256
+ *   workgroups in one dispatch (one workgroup per 128 queries or keys of a
+ *   head, times the split count where there is one).
+ * - Backward calls write each gradient with the strides of its input, so
+ *   the optimised side's inputs (all four for skl_backward_joint) must map
+ *   distinct elements to distinct addresses: a zero stride on an axis of
+ *   size > 1 (e.g. one K broadcast over the heads) or overlapping axes
+ *   return SKL_ERR_UNSUPPORTED.  The check takes the axes of size > 1 in
+ *   order of increasing stride and needs each stride to reach past the span
+ *   of the axes inside it (the d axis spans d elements).  The forward reads
+ *   its inputs only and accepts such layouts.
  * - Alignment: data pointers 16-byte aligned; b/h/n strides multiples of 8
  *   elements (bf16) or 4 elements (fp32).  Supported head dims: 64 and 128.
  * - Outputs must not alias inputs.

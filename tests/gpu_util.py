@@ -5,6 +5,10 @@ Tolerances (per-row KL and LSE, gradients as relative L2 per tensor and per head
   fp32 inputs: |dKL| <= 1e-5 |KL_ref| (+1e-7 abs when KL_ref is exactly 0),
                |dLSE| <= 1e-5, gradients <= 1e-4;
   bf16 inputs: |dKL| <= 2e-3 + 1e-2 |KL_ref|, |dLSE| <= 1e-3, gradients <= 1e-2.
+Gradients are also checked row by row (a query row of dQ, a key row of dK):
+the worst row's error, relative to the larger of that row's norm and the RMS
+row norm of the tensor, must stay within ROW_FACTOR times the tolerance, so
+that one wrong row cannot hide inside a tensor-wide relative L2.
 """
 import sys
 
@@ -18,6 +22,9 @@ TOL = {
     "f32": dict(kl_rel=1e-5, kl_abs=1e-7, lse=1e-5, grad=1e-4),
     "bf16": dict(kl_rel=1e-2, kl_abs=2e-3, lse=1e-3, grad=1e-2),
 }
+# Bound of the worst per-row error (relative to max(row norm, RMS row norm)),
+# in units of the relative-L2 tolerance.
+ROW_FACTOR = 3.0
 
 
 def say(msg: str) -> None:
@@ -62,6 +69,27 @@ def rel_l2(a, b) -> float:
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
 
 
+def worst_row_error(got, ref):
+    """(worst row error relative to max(row norm, RMS row norm), its row index);
+    rows are all axes but the last."""
+    g = np.asarray(got, np.float64).reshape(-1, np.shape(got)[-1])
+    r = np.asarray(ref, np.float64).reshape(-1, np.shape(ref)[-1])
+    rn = np.linalg.norm(r, axis=1)
+    rms = float(np.sqrt(np.mean(rn * rn)))
+    if rms == 0.0:
+        return 0.0, 0
+    e = np.linalg.norm(g - r, axis=1) / np.maximum(rn, rms)
+    i = int(e.argmax())
+    return float(e[i]), i
+
+
+def check_rows_grad(name, tol, got, ref):
+    """Per-row gradient bound (see ROW_FACTOR)."""
+    e, i = worst_row_error(got, ref)
+    assert e <= ROW_FACTOR * tol, f"{name}: row {i} error {e:.3e} > {ROW_FACTOR} x {tol}"
+    return e
+
+
 def check_grad(name, w, got, ref, per_head_axis=True):
     tol = TOL[w.dtype]["grad"]
     got = np.asarray(got, np.float64)
@@ -73,6 +101,13 @@ def check_grad(name, w, got, ref, per_head_axis=True):
         return
     e = rel_l2(got, ref)
     assert e <= tol, f"{name}: relative L2 error {e:.3e} > {tol}"
+    if per_head_axis and got.ndim == 4:
+        for b in range(got.shape[0]):
+            for h in range(got.shape[1]):
+                if np.linalg.norm(ref[b, h]) > 0:
+                    check_rows_grad(f"{name} head ({b},{h})", tol, got[b, h], ref[b, h])
+    else:
+        check_rows_grad(name, tol, got, ref)
     if per_head_axis and got.ndim == 4:
         for b in range(got.shape[0]):
             for h in range(got.shape[1]):

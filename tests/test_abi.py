@@ -164,3 +164,55 @@ def test_joint_backward_validation(lib):
     assert st == INVALID   # every gradient output is required
     st = lib.skl_backward_joint(ctypes.byref(s), *P, 0.1, 0.1, 2, A, A, A, A, A, A, A + 4, A, None, 0, None)
     assert st in (INVALID, UNSUPPORTED)
+
+
+def _student(lib, s, algo=0):
+    return lib.skl_backward_student(ctypes.byref(s), *P, 0.1, 0.1, 0, A, A, A, A, A, algo, None, 0, None)
+
+
+def _teacher(lib, s, algo=0):
+    return lib.skl_backward_teacher(ctypes.byref(s), *P, 0.1, 0.1, 0, A, A, A, A, A, A, algo, None, 0, None)
+
+
+def _joint(lib, s):
+    return lib.skl_backward_joint(ctypes.byref(s), *P, 0.1, 0.1, 0, A, A, A, A, A, A, A, A, None, 0, None)
+
+
+@pytest.mark.parametrize("tensor,axis,value", [
+    ("sk2", 1, 0),          # K2 broadcast over heads (expand)
+    ("sq2", 0, 0),          # Q2 broadcast over the batch (B = 2 below)
+    ("sk2", 2, 64),         # rows overlap (stride below the head dim 128)
+    ("sq2", 1, 256 * 64),   # heads interleaved into each other's rows
+])
+def test_backward_rejects_gradient_layouts_that_repeat_elements(lib, tensor, axis, value):
+    s = _shape(B=2)
+    getattr(s, tensor)[axis] = value
+    assert _student(lib, s) == UNSUPPORTED
+    assert "stride" in lib.skl_last_error().decode()
+    assert _joint(lib, s) == UNSUPPORTED
+
+
+def test_backward_accepts_bnhd_and_size_one_axes(lib):
+    from attention_kl_divergence_skl_amd import _disjoint_layout
+    # [B, N, H, d] storage viewed as [B, H, N, d].
+    assert _disjoint_layout((256 * 4 * 128, 128, 4 * 128), 2, 4, 256, 128)
+    # A size-1 axis may have any stride, 0 included.
+    assert _disjoint_layout((0, 256 * 128, 128), 1, 3, 256, 128)
+    assert not _disjoint_layout((256 * 128, 0, 128), 1, 3, 256, 128)
+    assert not _disjoint_layout((256 * 128, 256 * 128, 64), 1, 1, 256, 128)
+
+
+def test_dispatch_size_limit(lib):
+    # 2^20 heads x 16 query tiles = 2^24 workgroups > (2^32 - 1) / 256.
+    big = _shape(B=1, H=1 << 20, NQ=2048, NK=2048)
+    assert _fwd(lib, big) == UNSUPPORTED
+    assert "dispatch limit" in lib.skl_last_error().decode()
+    assert _student(lib, big) == UNSUPPORTED
+    assert _teacher(lib, big, algo=1) == UNSUPPORTED
+    assert _joint(lib, big) == UNSUPPORTED
+    # Split-K: 2^16 heads x 1 query tile x 256 splits.
+    sk = _shape(B=1, H=1 << 16, NQ=128, NK=65536)
+    need = lib.skl_forward_splitk_workspace_size(ctypes.byref(sk), 256)
+    st = lib.skl_forward_splitk(ctypes.byref(sk), *P, 0.1, 0.1, 0, 256, A, need, None)
+    assert st == UNSUPPORTED
+    assert "dispatch limit" in lib.skl_last_error().decode()

@@ -55,3 +55,30 @@ def test_autograd_frozen_teacher(gpu_lib):
     rq, rk = oracle.backward(x["q1"], x["k1"], x["q2"], x["k2"], w.scale1, w.scale2, True, g, "student")
     check_grad("frozen teacher dq2", w, q2.grad.float().cpu().numpy(), rq)
     check_grad("frozen teacher dk2", w, k2.grad.float().cpu().numpy(), rk)
+
+
+def test_autograd_key_broadcast_over_heads(gpu_lib):
+    """K1 shared by all heads through expand() (a stride of 0 on the head
+    axis): its gradient is the sum over heads of the per-head dK1.  The C ABI
+    itself rejects such a layout for the gradient it would write in place."""
+    w = W("ag_broadcast_k1", 2, 3, 200, 260, 64, 64, "bf16", True, synth.Recipe("iid", amp1=2.0))
+    say(f"[autograd] {w.name}")
+    x, t = to_device(w)
+    k1_shared = x["k1"][:, :1]                                     # [B, 1, NK, d1]
+    k1_full = np.ascontiguousarray(np.broadcast_to(k1_shared, x["k1"].shape))
+    base = torch.from_numpy(np.ascontiguousarray(k1_shared)).to(torch.bfloat16).cuda().requires_grad_(True)
+    k1 = base.expand(w.B, w.H, w.NK, w.d1)
+    assert k1.stride(1) == 0
+    q2 = t["q2"].clone().requires_grad_(True)
+    kl, _, _ = gpu_lib.attention_kl(t["q1"], k1, q2, t["k2"], w.scale1, w.scale2, True)
+    (kl * t["g"]).sum().backward()
+    torch.cuda.synchronize()
+    _, dk1 = oracle.backward(x["q1"], k1_full, x["q2"], x["k2"], w.scale1, w.scale2, True, x["g"], "teacher")
+    dq2, _ = oracle.backward(x["q1"], k1_full, x["q2"], x["k2"], w.scale1, w.scale2, True, x["g"], "student")
+    check_grad("broadcast k1 grad", w, base.grad.float().cpu().numpy(), dk1.sum(axis=1, keepdims=True))
+    check_grad("broadcast k1: dq2", w, q2.grad.float().cpu().numpy(), dq2)
+    kl2, l1, l2 = gpu_lib.skl_forward(t["q1"], k1.detach(), t["q2"], t["k2"], w.scale1, w.scale2, True)
+    with pytest.raises(gpu_lib.SklError) as e:
+        gpu_lib.skl_backward_teacher(t["q1"], k1.detach(), t["q2"], t["k2"], l1, l2, kl2, t["g"],
+                                     w.scale1, w.scale2, True)
+    assert e.value.status == 2

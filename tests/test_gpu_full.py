@@ -1,15 +1,17 @@
 """GPU parity at the full evaluation sizes, through the same entry points
 bench.py times.  The oracle checks sampled rows exactly (each row's KL, LSE
 and dQ only need that row), sampled key columns near the end of causal
-sequences (few rows see them), and, for every head, a property that holds at
-any size: the key gradients of a head sum to zero."""
+sequences (few rows see them), whole heads at 16K (every row and key column
+of dQ and dK), the first key columns at 64K (every query row sees them, so the
+dK kernel walks all query tiles for them), and, for every head, a property
+that holds at any size: the key gradients of a head sum to zero."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 from attention_kl_divergence_skl_amd import synth
-from tests.gpu_util import TOL, check_grad, rel_l2, say
+from tests.gpu_util import TOL, check_grad, check_rows_grad, rel_l2, say
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(600)]
 
@@ -54,7 +56,10 @@ def check_sampled_forward(w, kl, l1, l2, rows_seed=0):
             assert np.abs(got[k] - ref[k]).max() <= tol["lse"], f"{w.name} ({b},{h}) {k}"
 
 
-def check_sampled_backward(w, dq, dk, setting):
+def check_sampled_backward(w, dq, dk, setting, early_cols_head=None):
+    """Sampled dQ rows and trailing dK columns of a few heads; with
+    early_cols_head = (b, h), also key columns 0..31 of that head, which every
+    query row sees (the oracle materialises all rows for them)."""
     tol = TOL[w.dtype]["grad"]
     dq_np = dq.float()
     dk_np = dk.float()
@@ -63,13 +68,29 @@ def check_sampled_backward(w, dq, dk, setting):
         g = synth.head_grad(w, b, h)
         rows = sample_rows(w.NQ, 11 + h)
         rq = oracle.head_dq_rows(q1, k1, q2, k2, w.scale1, w.scale2, w.causal, g, setting, rows)
-        e = rel_l2(dq_np[b, h].cpu().numpy()[rows], rq)
+        got = dq_np[b, h].cpu().numpy()[rows]
+        e = rel_l2(got, rq)
         assert e <= tol, f"{w.name} ({b},{h}) sampled dQ ({setting}) rel L2 {e:.3e}"
+        check_rows_grad(f"{w.name} ({b},{h}) sampled dQ ({setting})", tol, got, rq)
         if w.causal:
             cols = np.arange(w.NK - 48, w.NK)
             rk = oracle.head_dk_cols(q1, k1, q2, k2, w.scale1, w.scale2, w.causal, g, setting, cols)
-            e = rel_l2(dk_np[b, h].cpu().numpy()[cols], rk)
+            got = dk_np[b, h].cpu().numpy()[cols]
+            e = rel_l2(got, rk)
             assert e <= tol, f"{w.name} ({b},{h}) sampled dK ({setting}) rel L2 {e:.3e}"
+            check_rows_grad(f"{w.name} ({b},{h}) trailing dK ({setting})", tol, got, rk)
+    if early_cols_head is not None:
+        b, h = early_cols_head
+        say(f"[full] {w.name} ({b},{h}) dK key columns 0..31 ({setting}) against the oracle")
+        q1, k1, q2, k2 = synth.head_inputs(w, b, h)
+        g = synth.head_grad(w, b, h)
+        cols = np.arange(32)
+        rk = oracle.head_dk_cols(q1, k1, q2, k2, w.scale1, w.scale2, w.causal, g, setting, cols)
+        got = dk_np[b, h].cpu().numpy()[cols]
+        e = rel_l2(got, rk)
+        assert e <= tol, f"{w.name} ({b},{h}) early dK ({setting}) rel L2 {e:.3e}"
+        er = check_rows_grad(f"{w.name} ({b},{h}) early dK ({setting})", tol, got, rk)
+        say(f"[full] early dK columns: rel L2 {e:.2e}, worst column {er:.2e}")
     # Property at any size: sum_j dK[j] = 0 for every head.
     s = dk.double().sum(dim=2).norm(dim=-1)
     f = dk.double().norm(dim=(2, 3))
@@ -120,6 +141,36 @@ def test_16k_forward_and_splitk(gpu_lib, store, causal):
         check_sampled_forward(w, skl_kl, s1, s2, rows_seed=splits)
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_16k_backward_full_head(gpu_lib, store, causal):
+    """Both backward settings at 16K x 16K, 32 heads: every row of dQ and every
+    key column of dK of one head against the oracle (early key columns walk
+    every query tile, late ones only the diagonal), sampled rows of two more
+    heads, and sum_j dK_j = 0 for all heads."""
+    w0, t = inputs(store, "n16k_h32_d128_corr05")
+    w = w0.with_(causal=causal)
+    kl, l1, l2 = gpu_lib.skl_forward(t["q1"], t["k1"], t["q2"], t["k2"], w.scale1, w.scale2, causal)
+    b, h = 0, w.H - 1
+    q1, k1, q2, k2 = synth.head_inputs(w, b, h)
+    g = synth.head_grad(w, b, h)
+    for setting in ("student", "teacher"):
+        say(f"[full] 16K {setting} backward causal={causal}")
+        if setting == "student":
+            dq, dk = gpu_lib.skl_backward_student(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, t["g"],
+                                                  w.scale1, w.scale2, causal)
+        else:
+            dq, dk = gpu_lib.skl_backward_teacher(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, kl, t["g"],
+                                                  w.scale1, w.scale2, causal)
+        torch.cuda.synchronize()
+        rq, rk = oracle.head_backward(q1, k1, q2, k2, w.scale1, w.scale2, causal, g, setting)
+        check_grad(f"16K ({b},{h}) dQ {setting} causal={causal}", w, dq[b, h].float().cpu().numpy(), rq,
+                   per_head_axis=False)
+        check_grad(f"16K ({b},{h}) dK {setting} causal={causal}", w, dk[b, h].float().cpu().numpy(), rk,
+                   per_head_axis=False)
+        check_sampled_backward(w, dq, dk, setting)
+        del dq, dk
+
+
 def test_causal_64k_forward_student_teacher(gpu_lib, store):
     w, t = inputs(store, "causal_64k_h32_d128_q1x4")
     say("[full] causal 64K forward")
@@ -136,7 +187,7 @@ def test_causal_64k_forward_student_teacher(gpu_lib, store):
     dq, dk = gpu_lib.skl_backward_teacher(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, kl, t["g"],
                                           w.scale1, w.scale2, True)
     torch.cuda.synchronize()
-    check_sampled_backward(w, dq, dk, "teacher")
+    check_sampled_backward(w, dq, dk, "teacher", early_cols_head=(0, 5))
 
 
 def test_causal_128k_indexer_student(gpu_lib, store):
