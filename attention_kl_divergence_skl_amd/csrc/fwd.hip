@@ -42,8 +42,15 @@ namespace skl {
 constexpr float kNoKey = -1e30f;
 // Largest block sum kept against a stale running maximum (2^64).
 constexpr float kFastCap = 18446744073709551616.0f;
+// Update modes of the forward's online statistics (see update in fwd_kernel).
+constexpr int kDeferred = 0, kChecked = 1, kFirst = 2;
 
-template <typename T, int D1, int D2, bool CAUSAL, bool SPLIT>
+// Marker written into a row's KL (plain forward) or acc partial (split-K) by
+// the main pass when that row needs the fixup pass: a NaN with a payload of
+// its own, compared as bits (the file is compiled without NaN semantics).
+constexpr uint32_t kRedoMark = 0x7fc0dbadu;
+
+template <typename T, int D1, int D2, bool CAUSAL, bool SPLIT, bool FIXUP>
 __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(const FwdParams p) {
   using M = Mfma<T>;
   using frag = typename M::frag;
@@ -83,6 +90,19 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(c
   const int64_t qw0 = (int64_t)qt * kFwdBQ + wave * 32;  // first query of this wave
   const int64_t qi = qw0 + col;                           // this lane's query
   const bool qvalid = qi < p.NQ;
+  // Where the main pass left its marker for this row (KL, or the split's acc).
+  auto mark_slot = [&]() -> float* {
+    if (SPLIT) {
+      const int64_t BH = gridDim.x / ((int64_t)p.num_qtiles * p.splits);
+      return p.part + 4 * BH * p.splits * p.NQ + (bh * p.splits + split) * p.NQ + qi;
+    }
+    return p.kl + bh * p.NQ + qi;
+  };
+  if (FIXUP) {
+    // Only tiles with a marked row are recomputed; the others leave at once.
+    const bool marked = half == 0 && qvalid && __float_as_uint(*mark_slot()) == kRedoMark;
+    if (!__syncthreads_or(marked ? 1 : 0)) return;
+  }
 
   const char* const q1p = (const char*)p.q1 + (b * p.sq1.b + h * p.sq1.h) * ESZ;
   const char* const q2p = (const char*)p.q2 + (b * p.sq2.b + h * p.sq2.h) * ESZ;
@@ -116,20 +136,39 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(c
 
   // Key tiles are loaded straight into a double-buffered LDS ring: the loads
   // of tile i+1 are in flight while tile i is computed; one barrier per tile.
+  // A full tile's load instructions take a uniform base (row j0 + 16 k for
+  // 256-byte rows, + 32 k for 128-byte rows) in scalar registers plus one
+  // loop-invariant lane offset per side: the swizzle repeats every 16 rows,
+  // so all of a wave's instructions share that offset.  The ragged last tile
+  // takes the clamping loader.
   const int64_t rs1 = p.sk1.n * ESZ, rs2 = p.sk2.n * ESZ;
+  constexpr int RPI1 = 1024 / RB1, RPI2 = 1024 / RB2;  // rows per load instruction
+  const int r01 = wave * RPI1 + lane / T1::CPR, r02 = wave * RPI2 + lane / T2::CPR;
+  const unsigned lo1 = (unsigned)(r01 * (int)rs1 + (((lane % T1::CPR) ^ T1::swz(r01)) * 16));
+  const unsigned lo2 = (unsigned)(r02 * (int)rs2 + (((lane % T2::CPR) ^ T2::swz(r02)) * 16));
   auto fetch = [&](int st, int j0) {
-    tile_load_async<BK, RB1>(sK1(st), k1p, rs1, j0, NK, wave, lane);
-    tile_load_async<BK, RB2>(sK2(st), k2p, rs2, j0, NK, wave, lane);
+    if (j0 + BK <= NK) {
+      // Fresh copies of the lane offsets here, so that they are not hoisted
+      // as 64-bit values (which loses the scalar-base form of the loads).
+      unsigned o1 = lo1, o2 = lo2;
+      asm volatile("" : "+v"(o1), "+v"(o2));
+#pragma unroll
+      for (int k = 0; k < BK / RPI1 / 4; ++k)
+        global_load_lds16(uniform_ptr(k1p + (int64_t)(j0 + 4 * k * RPI1) * rs1) + o1, sK1(st) + (wave + 4 * k) * 1024);
+#pragma unroll
+      for (int k = 0; k < BK / RPI2 / 4; ++k)
+        global_load_lds16(uniform_ptr(k2p + (int64_t)(j0 + 4 * k * RPI2) * rs2) + o2, sK2(st) + (wave + 4 * k) * 1024);
+    } else {
+      tile_load_async<BK, RB1>(sK1(st), k1p, rs1, j0, NK, wave, lane);
+      tile_load_async<BK, RB2>(sK2(st), k2p, rs2, j0, NK, wave, lane);
+    }
   };
 
   const float c1 = p.c1, c2 = p.c2;
   // Running maxima in base-2 units start at the finite kNoKey ("no key seen"),
   // so that every shift and correction factor below is finite.
   float m1 = kNoKey, m2 = kNoKey, l1 = 0.f, l2 = 0.f, acc = 0.f;
-
-  if (nsteps > 0) fetch(0, kbeg);
-  wait_vm();
-  __syncthreads();
+  bool over = false;  // a kept-maximum block exceeded the cap (deferred check)
 
   // Per-lane byte offsets of the A fragments inside a 32-row block: the
   // swizzle repeats every 16 rows, so block kb of stage st is at the constant
@@ -167,17 +206,25 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(c
 
   // Online update of the row statistics with one block whose first key is jb.
   //
-  // Most blocks keep the running maxima: the block is first summed against the
-  // current (m1, m2), and that result is kept whenever both of its sums stay at
-  // or below kFastCap = 2^64, which bounds every term by 2^64 (far from fp32
-  // overflow even after summing 2^20 blocks).  A stale maximum only makes the
-  // terms larger, never smaller, so nothing underflows that the exact update
-  // would keep; the sums are the same quantities in another base-2 unit.  Only
-  // when a lane's sums exceed the cap (or no key has been seen yet: m is then
-  // kNoKey and the terms overflow) does that lane take the exact update with a
-  // new block maximum and the correction factors.  The block maximum, the two
-  // correction exponentials and the rescales are thus off the common path.
-  auto update = [&](f32x16& s1, f32x16& s2, int jb) __attribute__((always_inline)) {
+  // Most blocks keep the running maxima: the block is summed against the
+  // current (m1, m2), and that result is valid whenever both of its sums stay
+  // at or below kFastCap = 2^64, which bounds every term by 2^64 (far from
+  // fp32 overflow even after summing 2^20 blocks).  A stale maximum only makes
+  // the terms larger, never smaller, so nothing underflows that the exact
+  // update would keep; the sums are the same quantities in another base-2
+  // unit.  The exact update of the online formula (new block maximum,
+  // correction factors, rescale) is needed only when a block exceeds the cap
+  // or no key has been seen yet.  Modes:
+  //   kFirst     the first block of the key range: always the exact update
+  //              (it sets the maxima from the block's own logits);
+  //   kDeferred  every later block on the main pass: the kept-maximum sums
+  //              are committed without a branch and a block over the cap only
+  //              sets `over`; the workgroup then repeats its key range in
+  //              kChecked mode (rare: logits rising by more than ~64 bits of
+  //              range after the first block);
+  //   kChecked   per block, the exact update only where the cap is exceeded.
+  auto update = [&](auto modec, f32x16& s1, f32x16& s2, int jb) __attribute__((always_inline)) {
+    constexpr int mode = decltype(modec)::value;
     const bool need_mask = jb > mask_after;
     if (need_mask) {
       // Key jb + ro is visible iff ro < NK - jb and (causal) ro <= qi + off - jb.
@@ -230,14 +277,10 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(c
       accd = (pa[0] + pa[1]) + (pa[2] + pa[3]);
     };
 
-    float sum1, sum2, accd;
-    block_sums(m1, m2, sum1, sum2, accd);
-    // t1 - t2 = (u1 - u2) + (m1 - m2): the per-row part is added once per block.
-    float nl1 = l1 + sum1, nl2 = l2 + sum2, nacc = acc + fmaf(m1 - m2, sum1, accd);
-    if (!(sum1 <= kFastCap && sum2 <= kFastCap)) {
-      // Block maxima of the raw logits as a tree of 3-input maxima, scaled
-      // afterwards (the scales are positive) and joined with the running
-      // maxima; a lane whose keys are all masked keeps its maxima.
+    // Exact update: block maxima of the raw logits as a tree of 3-input
+    // maxima, scaled afterwards (the scales are positive) and joined with the
+    // running maxima (a lane whose keys are all masked keeps its maxima).
+    auto exact = [&]() __attribute__((always_inline)) {
       auto max3 = [](float a, float b, float c) __attribute__((always_inline)) { return fmaxf(fmaxf(a, b), c); };
       auto tree = [&](const f32x16& v) __attribute__((always_inline)) {
         const float b0 = max3(max3(v[0], v[1], v[2]), max3(v[3], v[4], v[5]), max3(v[6], v[7], v[8]));
@@ -246,40 +289,77 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(c
       };
       const float m1n = fmaxf(tree(s1) * c1, m1), m2n = fmaxf(tree(s2) * c2, m2);
       const float a1f = exp2_hw(m1 - m1n), a2f = exp2_hw(m2 - m2n);
+      float sum1, sum2, accd;
       block_sums(m1n, m2n, sum1, sum2, accd);
-      nl1 = fmaf(l1, a1f, sum1);
-      nl2 = fmaf(l2, a2f, sum2);
-      nacc = fmaf(acc, a1f, fmaf(m1n - m2n, sum1, accd));
+      l1 = fmaf(l1, a1f, sum1);
+      l2 = fmaf(l2, a2f, sum2);
+      acc = fmaf(acc, a1f, fmaf(m1n - m2n, sum1, accd));
       m1 = m1n;
       m2 = m2n;
+    };
+
+    if constexpr (mode == kFirst) {
+      exact();
+    } else {
+      float sum1, sum2, accd;
+      block_sums(m1, m2, sum1, sum2, accd);
+      const bool fits = sum1 <= kFastCap && sum2 <= kFastCap;
+      // t1 - t2 = (u1 - u2) + (m1 - m2): the per-row part is added once per block.
+      const float nl1 = l1 + sum1, nl2 = l2 + sum2, nacc = acc + fmaf(m1 - m2, sum1, accd);
+      if constexpr (mode == kDeferred) {
+        over |= !fits;
+        l1 = nl1;
+        l2 = nl2;
+        acc = nacc;
+      } else {
+        if (fits) {
+          l1 = nl1;
+          l2 = nl2;
+          acc = nacc;
+        } else {
+          exact();
+        }
+      }
     }
-    l1 = nl1;
-    l2 = nl2;
-    acc = nacc;
   };
 
   // Block-level software pipeline: the MFMAs of the next 32-key block are
   // issued before the online update of the current one (across the tile
   // barrier too), so each wave keeps matrix work in flight while its VALU
   // runs the softmax.  Blocks past the wave's last visible key are skipped.
+  // The first step is peeled so that only its first block takes kFirst.  The
+  // main pass commits later blocks in kDeferred mode and marks the rows that
+  // went over the cap; the fixup pass (FIXUP) repeats such tiles in kChecked
+  // mode.
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using First = std::integral_constant<int, kFirst>;
+  using Later = std::integral_constant<int, FIXUP ? kChecked : kDeferred>;
   f32x16 sa1, sa2, sb1, sb2;  // block 0 / block 1 of the current tile
-  auto step = [&](auto stc, int it) {
+  auto step = [&](auto stc, int it, auto mode0) {
     constexpr int st = decltype(stc)::value;
     const int j0 = kbeg + it * BK;
     if (it + 1 < nsteps) fetch(st ^ 1, j0 + BK);
     const bool live0 = j0 <= wave_kmax, live1 = j0 + 32 <= wave_kmax;
     if (live1) logits(stc, 1, sb1, sb2);
-    if (live0) update(sa1, sa2, j0);
+    if (live0) update(mode0, sa1, sa2, j0);
     wait_vm();
     __syncthreads();
     if (it + 1 < nsteps && j0 + BK <= wave_kmax) logits(std::integral_constant<int, st ^ 1>{}, 0, sa1, sa2);
-    if (live1) update(sb1, sb2, j0 + 32);
+    if (live1) update(Later{}, sb1, sb2, j0 + 32);
   };
-  if (nsteps > 0 && kbeg <= wave_kmax) logits(std::integral_constant<int, 0>{}, 0, sa1, sa2);
-  for (int it = 0; it < nsteps; it += 2) {
-    step(std::integral_constant<int, 0>{}, it);
-    if (it + 1 < nsteps) step(std::integral_constant<int, 1>{}, it + 1);
+  if (nsteps > 0) fetch(0, kbeg);
+  wait_vm();
+  __syncthreads();
+  if (nsteps > 0) {
+    if (kbeg <= wave_kmax) logits(I0{}, 0, sa1, sa2);
+    step(I0{}, 0, First{});
   }
+  for (int it = 1; it < nsteps; it += 2) {
+    step(I1{}, it, Later{});
+    if (it + 1 < nsteps) step(I0{}, it + 1, Later{});
+  }
+  const bool redo = over || __shfl_xor(over ? 1 : 0, 32) != 0;
 
   // Merge the two lane halves (disjoint key subsets of the same row).
   const float om1 = __shfl_xor(m1, 32), ol1 = __shfl_xor(l1, 32);
@@ -302,13 +382,13 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void fwd_kernel(c
       dst[stride_f] = L1;
       dst[2 * stride_f] = (L2 > 0.f) ? M2 : neg_inf();
       dst[3 * stride_f] = L2;
-      dst[4 * stride_f] = ACC;
+      dst[4 * stride_f] = redo ? __uint_as_float(kRedoMark) : ACC;
     } else {
       const float lg1 = log2f(L1), lg2 = log2f(L2);
       const int64_t o = bh * p.NQ + qi;
       p.lse1[o] = kLn2 * (M1 + lg1);
       p.lse2[o] = kLn2 * (M2 + lg2);
-      p.kl[o] = kLn2 * (ACC / L1 + (M2 - M1) + (lg2 - lg1));
+      p.kl[o] = redo ? __uint_as_float(kRedoMark) : kLn2 * (ACC / L1 + (M2 - M1) + (lg2 - lg1));
     }
   }
 }
@@ -345,10 +425,15 @@ __global__ __launch_bounds__(256) void reduce_kernel(const ReduceParams p) {
 
 namespace {
 
+// The main pass, then the fixup pass over the same tiles (most of its
+// workgroups find no marked row and leave at once).
 template <typename T, int D1, int D2, bool C, bool S>
 hipError_t run_fwd(const FwdParams& p, int64_t BH, hipStream_t s) {
   const int64_t grid = BH * p.num_qtiles * (S ? p.splits : 1);
-  hipLaunchKernelGGL((fwd_kernel<T, D1, D2, C, S>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL((fwd_kernel<T, D1, D2, C, S, false>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((fwd_kernel<T, D1, D2, C, S, true>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 

@@ -147,6 +147,23 @@ __device__ __forceinline__ void tile_load_async(char* tile, const char* g, int64
   }
 }
 
+// A pointer that has the same value in every lane of the wave, made visibly
+// uniform (held in scalar registers), so that address arithmetic on it stays
+// scalar and memory instructions can take it as their scalar base.
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
+}
+
+// One direct global -> LDS load of 16 bytes per lane (gfx950
+// global_load_lds_dwordx4): lane i writes at lds + 16 i.
+__device__ __forceinline__ void global_load_lds16(const char* g, char* lds) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
 // A condition that has the same value in every lane of the wave, made visibly
 // uniform: branches on it become scalar branches instead of per-lane
 // predication (the compiler cannot tell that values derived from tid >> 6 are

@@ -207,6 +207,23 @@ def test_rising_logits_overtake_running_max(gpu_lib, causal):
     check_grad(f"{w.name} dK2", w, grad_to_np(dk), rk)
 
 
+@pytest.mark.parametrize("splits", [2, 5])
+@pytest.mark.parametrize("causal", [False, True])
+def test_rising_logits_split_k(gpu_lib, splits, causal):
+    """The rising-logits inputs through split-K + reduce: splits whose later
+    blocks overtake the first block's maximum take the per-block exact update
+    on the second pass, through the split's own partials."""
+    w = W("rising_split", 1, 2, 256, 640, 64, 64, "bf16", causal,
+          synth.Recipe("iid", amp1=6.0, amp2=6.0, kramp=8.0))
+    say(f"[rising logits, split-K {splits}] causal={causal}")
+    x, t = to_device(w)
+    ws, n = gpu_lib.skl_forward_splitk(t["q1"], t["k1"], t["q2"], t["k2"], w.scale1, w.scale2, causal, splits)
+    kl, l1, l2 = gpu_lib.skl_reduce(ws, n, w.B, w.H, w.NQ)
+    torch.cuda.synchronize()
+    got = {"kl": kl.cpu().numpy(), "lse1": l1.cpu().numpy(), "lse2": l2.cpu().numpy()}
+    check_rows(f"rising split{splits}", w, got, oracle_forward(w, x))
+
+
 @pytest.mark.parametrize("splits", [1, 2, 3, 4, 8])
 @pytest.mark.parametrize("causal", [False, True])
 def test_splitk_matches_oracle_and_plain_forward(gpu_lib, splits, causal):
