@@ -37,23 +37,9 @@ namespace skl {
 
 namespace {
 
-// dS of one accumulator element (dK kernel, whose accumulator rows are queries
-// with their own g) from the two logits (raw dot products) and
-// the row constants L_k = LSE_k log2 e and, for the student, ga = g; for the
-// teacher ga = g ln2 and gb = g KL, so that
-//   student: g (P2 - P1)                      = ga (2^u2 - 2^u1)
-//   teacher: g P1 (ln2 (u1 - u2) - KL)        = 2^u1 (ga (u1 - u2) - gb)
-template <bool TEACHER>
-__device__ __forceinline__ float dS_of(float s1, float s2, float c1, float c2, float L1, float L2, float ga,
-                                       float gb) {
-  const float u1 = fmaf(s1, c1, -L1);
-  const float u2 = fmaf(s2, c2, -L2);
-  if (TEACHER) return exp2_hw(u1) * fmaf(ga, u1 - u2, -gb);
-  return ga * (exp2_hw(u2) - exp2_hw(u1));
-}
-
-// sign(g) dS of one accumulator element (dQ kernel, one query per lane) from
-// the two logits (raw dot products) and two row constants that fold the upstream gradient into the exponents.  With
+// sign(g) dS of one accumulator element from the two logits (raw dot
+// products) and two row constants that fold the upstream gradient into the
+// exponents.  With
 // u_k = t_k - LSE_k log2 e (so P_k = 2^u_k), ga = g (student) or g ln2
 // (teacher) and k = log2 |ga|:
 //   student: g (P2 - P1) = sign(g) (2^(u2 + k) - 2^(u1 + k))
@@ -62,7 +48,9 @@ __device__ __forceinline__ float dS_of(float s1, float s2, float c1, float c2, f
 // so the row constants are A1 = L1 - k and A2 = L2 - k (student) or
 // L2 - k - KL log2 e (teacher), and the element needs no multiply by g.  A
 // row with g = 0 gets A1 = kZeroRow (and a finite A2), whose exponential is 0.
-// The dQ kernel applies the sign to each finished dQ row.
+// The dQ kernel (one query per lane) applies the sign to each finished dQ
+// row; the dK kernel (whose accumulator rows are queries) multiplies dS by it
+// in the tiles that have a row with g < 0.
 template <bool TEACHER>
 __device__ __forceinline__ float dS_abs(float s1, float s2, float c1, float c2, float A1, float A2) {
   const float w1 = fmaf(s1, c1, -A1);
@@ -114,13 +102,23 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dk_kerne
   using T2 = SwzTile<RB2>;
   using TG = SwzTile<RBG>;
 
-  __shared__ __attribute__((aligned(1024))) char sQ1[2][BQ * RB1];
-  __shared__ __attribute__((aligned(1024))) char sQ2[2][BQ * RB2];
-  __shared__ __attribute__((aligned(16))) float sVec[2][4][BQ];  // L1, L2 (base 2), ga, gb (see dS_of)
+  // The ring's two stages stay one [2][...] array here: as separate variables
+  // (which lets the compiler see that reads of one stage do not wait for the
+  // loads in flight into the other, as in the forward and dQ kernels) this
+  // kernel spills heavily at 256 VGPRs, and measured slower.
+  __shared__ __attribute__((aligned(1024))) char sQ1x[2][BQ * RB1];
+  __shared__ __attribute__((aligned(1024))) char sQ2x[2][BQ * RB2];
+  // Per query row of a tile: A1, A2 (row constants of dS_abs) and sign(g);
+  // plus a flag per stage: some row of the tile has g < 0.
+  __shared__ __attribute__((aligned(16))) float sVa[3][BQ], sVb[3][BQ];
+  __shared__ int sNeg[2];
+  auto sQ1 = [&](int st) __attribute__((always_inline)) -> char* { return sQ1x[st]; };
+  auto sQ2 = [&](int st) __attribute__((always_inline)) -> char* { return sQ2x[st]; };
+  auto sVec = [&](int st) __attribute__((always_inline)) -> float(*)[BQ] { return st ? sVb : sVa; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int half = lane >> 5, col = lane & 31;
 
   const int64_t t = xcd_remap(blockIdx.x, gridDim.x);
@@ -155,28 +153,39 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dk_kerne
   const int64_t nsteps = (p.NQ - qbeg + BQ - 1) / BQ;
 
   // Query tiles go straight into a double-buffered LDS ring (loads of step
-  // i+1 in flight during step i); the four per-row constants go through one
-  // register per thread (wave w holds constant w of the tile's 64 rows).  The
-  // fetch only loads them: any arithmetic on a loaded value would make the
+  // i+1 in flight during step i).  The row values of the tile (LSE1, LSE2, g
+  // and, for the teacher, KL) are loaded by the first wave, one row per lane;
+  // the fetch only loads them: any arithmetic on a loaded value would make the
   // wave wait for all its outstanding loads, the next tile's included, in the
-  // middle of the step, so the scaling happens at the stash after the step.
-  static_assert(4 * BQ == kThreads, "one wave per row constant");
-  const int which = tid / BQ, vrow = tid % BQ;  // which == wave
-  const float* const vsrc = which == 0 ? p.lse1 : which == 1 ? p.lse2 : p.dkl;
-  float pv = 0.f, pv2 = 0.f;
+  // middle of the step, so the row constants are formed at the stash after
+  // the step.  |g| goes into the exponents (see dS_abs); its sign multiplies
+  // dS only in the rare tiles that have a row with g < 0.
+  static_assert(BQ == 64, "one lane of the first wave per query row");
+  float pl1 = 0.f, pl2 = 0.f, pg = 0.f, pkl = 0.f;
   auto fetch = [&](int st, int64_t q0) {
-    tile_load_async<BQ, RB1>(sQ1[st], q1p, p.sq1.n * ESZ, (int)q0, (int)p.NQ, wave, lane);
-    tile_load_async<BQ, RB2>(sQ2[st], q2p, p.sq2.n * ESZ, (int)q0, (int)p.NQ, wave, lane);
-    const int64_t q = q0 + vrow;
-    const int64_t o = bh * p.NQ + (q < p.NQ ? q : p.NQ - 1);  // rows past N_Q are zeroed at the stash
-    pv = vsrc[o];
-    if (TEACHER && which == 3) pv2 = p.kl[o];
+    tile_load_async<BQ, RB1>(sQ1(st), q1p, p.sq1.n * ESZ, (int)q0, (int)p.NQ, wave, lane);
+    tile_load_async<BQ, RB2>(sQ2(st), q2p, p.sq2.n * ESZ, (int)q0, (int)p.NQ, wave, lane);
+    if (wave == 0) {
+      const int64_t q = q0 + lane;
+      const int64_t o = bh * p.NQ + (q < p.NQ ? q : p.NQ - 1);  // rows past N_Q are zeroed at the stash
+      pl1 = p.lse1[o];
+      pl2 = p.lse2[o];
+      pg = p.dkl[o];
+      if (TEACHER) pkl = p.kl[o];
+    }
   };
   auto stash = [&](int st, int64_t q0) {
-    float v;
-    if (which == 3) v = TEACHER ? pv * pv2 : 0.f;                 // g KL (teacher)
-    else v = pv * (which == 2 ? (TEACHER ? kLn2 : 1.f) : kLog2e);  // L1, L2 (base 2), ga
-    sVec[st][which][vrow] = (q0 + vrow < p.NQ) ? v : 0.f;
+    if (wave == 0) {
+      const bool valid = q0 + lane < p.NQ;
+      float A1 = kZeroRow, A2 = TEACHER ? 0.f : kZeroRow;
+      if (valid) row_consts<TEACHER>(pl1, pl2, pkl, pg, A1, A2);
+      float(*v)[BQ] = sVec(st);
+      v[0][lane] = A1;
+      v[1][lane] = A2;
+      v[2][lane] = (valid && pg < 0.f) ? -1.f : 1.f;
+      const bool neg = __builtin_amdgcn_ballot_w64(valid && pg < 0.f) != 0;
+      if (lane == 0) sNeg[st] = neg ? 1 : 0;
+    }
   };
 
   if (nsteps > 0) {
@@ -201,9 +210,8 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dk_kerne
     const int64_t q0 = qbeg + it * BQ;
     if (it + 1 < nsteps) fetch(st ^ 1, q0 + BQ);  // next tile in flight during this step
 
-    const char* qg = TEACHER ? &sQ1[0][0] : &sQ2[0][0];  // addressed through xg below (bf16) ...
-    const char* qgs = TEACHER ? &sQ1[st][0] : &sQ2[st][0];  // ... or directly (fp32)
-    const SwzAddr<RBG> xg = adg.shifted(st * BQ * RBG);
+    const char* qgs = TEACHER ? sQ1(st) : sQ2(st);  // gradient operand tile of this stage
+    const bool neg_tile = __builtin_amdgcn_readfirstlane(sNeg[st]) != 0;
 #pragma unroll
     for (int qb = 0; qb < BQ / 32; ++qb) {
       const int64_t qb0 = q0 + 32 * qb;
@@ -222,8 +230,8 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dk_kerne
       constexpr int NCM = NC1 > NC2 ? NC1 : NC2;
       frag pa1[2], pa2[2];
       auto ld = [&](int c, int slot) __attribute__((always_inline)) {
-        if (c < NC1) pa1[slot] = M::load(&sQ1[st][T1::off(qrow, (c * KC + half * EPL) * ESZ)]);
-        if (c < NC2) pa2[slot] = M::load(&sQ2[st][T2::off(qrow, (c * KC + half * EPL) * ESZ)]);
+        if (c < NC1) pa1[slot] = M::load(&sQ1(st)[T1::off(qrow, (c * KC + half * EPL) * ESZ)]);
+        if (c < NC2) pa2[slot] = M::load(&sQ2(st)[T2::off(qrow, (c * KC + half * EPL) * ESZ)]);
       };
       ld(0, 0);
 #pragma unroll
@@ -253,22 +261,29 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void bwd_dk_kerne
         frag bq[NCB];
         if constexpr (EPL != 1) {
 #pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) bq[cb] = xg.trfrag(qg, (32 * qb + run * KC) * RBG, cb);
+          for (int cb = 0; cb < NCB; ++cb) bq[cb] = adg.trfrag(qgs, (32 * qb + run * KC) * RBG, cb);
           __builtin_amdgcn_sched_barrier(0);
         }
-        float cst[4][8];
-#pragma unroll
-        for (int which = 0; which < (TEACHER ? 4 : 3); ++which) {
-          const float4* v = reinterpret_cast<const float4*>(&sVec[st][which][32 * qb + 16 * run + 8 * half]);
+        auto row8 = [&](int which, float (&dst)[8]) __attribute__((always_inline)) {
+          const float4* v = reinterpret_cast<const float4*>(&sVec(st)[which][32 * qb + 16 * run + 8 * half]);
           const float4 x0 = v[0], x1 = v[1];
-          cst[which][0] = x0.x; cst[which][1] = x0.y; cst[which][2] = x0.z; cst[which][3] = x0.w;
-          cst[which][4] = x1.x; cst[which][5] = x1.y; cst[which][6] = x1.z; cst[which][7] = x1.w;
-        }
+          dst[0] = x0.x; dst[1] = x0.y; dst[2] = x0.z; dst[3] = x0.w;
+          dst[4] = x1.x; dst[5] = x1.y; dst[6] = x1.z; dst[7] = x1.w;
+        };
+        float a1[8], a2[8];
+        row8(0, a1);
+        row8(1, a2);
         float ds[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int r = 8 * run + i;
-          ds[i] = dS_of<TEACHER>(s1[r], s2[r], c1, c2, cst[0][i], cst[1][i], cst[2][i], TEACHER ? cst[3][i] : 0.f);
+          ds[i] = dS_abs<TEACHER>(s1[r], s2[r], c1, c2, a1[i], a2[i]);
+        }
+        if (neg_tile) {
+          float sg[8];
+          row8(2, sg);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) ds[i] *= sg[i];
         }
         if (need_mask) {
 #pragma unroll
