@@ -23,6 +23,7 @@ __all__ = [
     "skl_backward_joint_workspace_size",
     "skl_forward_splitk_workspace_size", "skl_backward_workspace_size",
     "skl_version", "skl_set_kernel_events", "LIB_PATH",
+    "skl_forward_splitk_noalloc", "skl_noalloc_scratch_bytes",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libstreamkl.so")
@@ -68,6 +69,8 @@ _SIGS = {
     "skl_backward_joint_workspace_size": (_SZ, [_SP]),
     "skl_backward_joint": (_I, [_SP, _P, _P, _P, _P, _F, _F, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "skl_recommended_splits": (_I, [_SP, _I, _I]),
+    "skl_noalloc_scratch_bytes": (_SZ, []),
+    "skl_forward_splitk_noalloc": (_I, [_SP, _P, _P, _P, _P, _F, _F, _I, _I, _P, _P, _P, _P]),
     "skl_status_string": (ctypes.c_char_p, [_I]),
     "skl_last_error": (ctypes.c_char_p, []),
     "skl_version": (_I, []),
@@ -226,6 +229,33 @@ def skl_forward_splitk(q1, k1, q2, k2, scale1=None, scale2=None, causal: bool = 
                                      int(causal), int(num_splits), _ptr(ws), ws.numel() * ws.element_size(),
                                      _stream(q1)))
     return ws, int(num_splits)
+
+
+def skl_forward_splitk_noalloc(q1, k1, q2, k2, scale1=None, scale2=None, causal: bool = False,
+                               num_splits: Optional[int] = None, out=None):
+    """(kl, lse1, lse2) through split-K + reduce with the partials in the
+    library's static scratch array (no workspace).  ``out`` may hold three
+    preallocated contiguous fp32 [B, H, N_Q] tensors, so that the call itself
+    allocates nothing."""
+    import torch
+
+    _check_device(q1, k1, q2, k2)
+    s = make_shape(q1, k1, q2, k2)
+    s1, s2 = _scales(q1, q2, scale1, scale2)
+    if num_splits is None:
+        num_splits = skl_recommended_splits(q1, k1, q2, k2, causal)
+    if out is None:
+        out = [torch.empty((s.B, s.H, s.NQ), dtype=torch.float32, device=q1.device) for _ in range(3)]
+    for t, n in zip(out, ("kl", "lse1", "lse2")):
+        _rowvec(t, s.B, s.H, s.NQ, n)
+    _check(load().skl_forward_splitk_noalloc(ctypes.byref(s), _ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), s1, s2,
+                                             int(causal), int(num_splits), _ptr(out[0]), _ptr(out[1]),
+                                             _ptr(out[2]), _stream(q1)))
+    return tuple(out)
+
+
+def skl_noalloc_scratch_bytes() -> int:
+    return int(load().skl_noalloc_scratch_bytes())
 
 
 def skl_reduce(ws, num_splits: int, B: int, H: int, NQ: int):

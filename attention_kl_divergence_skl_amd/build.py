@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libstreamkl.so")
-SOURCES = ["api.cpp", "fwd.hip", "bwd.hip", "bwd_split.hip", "bwd_joint.hip"]
+SOURCES = ["api.cpp", "fwd.hip", "bwd.hip", "bwd_split.hip", "bwd_joint.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 ops (v_pk_fma_f32 & co.) are switched off for all device code.

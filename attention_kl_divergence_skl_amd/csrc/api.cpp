@@ -205,6 +205,20 @@ int64_t split_len_for(int64_t nk, int splits) {
 
 }  // namespace
 
+namespace skl {
+
+skl_status set_error(skl_status status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+}  // namespace skl
+
 extern "C" {
 
 int skl_version(void) { return 100; }

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/streamkl.h"
+
 namespace skl {
 
 // Geometry fixed by the kernels.
@@ -109,5 +111,9 @@ hipError_t launch_backward_split(const BwdParams& p, int dtype, int d1, int d2, 
 hipError_t launch_backward_joint(const BwdParams& p, int dtype, int d1, int d2, bool causal, int64_t BH,
                                  hipStream_t s, void (*between)(hipStream_t));
 hipError_t launch_convert(const ConvertParams& p, int dtype, hipStream_t s);
+
+// Records a printf-style message as this thread's last error (skl_last_error)
+// and returns `status` (api.cpp).
+skl_status set_error(skl_status status, const char* fmt, ...);
 
 }  // namespace skl

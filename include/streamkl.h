@@ -144,6 +144,26 @@ skl_status skl_reduce(const skl_shape* shape, int num_splits, const void* ws, si
                       float* kl, float* lse1, float* lse2, hipStream_t stream);
 
 /*
+ * Allocation-free split-K forward, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Computes what skl_forward_splitk followed by skl_reduce
+ * computes (outputs kl, lse1, lse2 as skl_forward), with the split partials in
+ * a static device array of skl_noalloc_scratch_bytes() bytes (32 MiB) that the
+ * library holds on each GPU it runs on until the process ends, instead of a
+ * caller workspace.  Allocates nothing.  A shape whose partials
+ * (20 * B * H * N_Q * num_splits bytes) exceed the array returns
+ * SKL_ERR_UNSUPPORTED before anything is enqueued; other errors as
+ * skl_forward_splitk and skl_reduce.  Every call on one GPU uses that GPU's
+ * array: calls that overlap on one GPU (several streams or host threads)
+ * race, and the caller must serialise them.
+ */
+size_t skl_noalloc_scratch_bytes(void);
+skl_status skl_forward_splitk_noalloc(const skl_shape* shape,
+                                      const void* q1, const void* k1, const void* q2, const void* k2,
+                                      float scale1, float scale2, int causal, int num_splits,
+                                      float* kl, float* lse1, float* lse2, hipStream_t stream);
+
+/*
  * Workspace bytes a backward call with algorithm `algo` uses, with
  * d = d2 (teacher == 0) or d1 (teacher != 0):
  *  SKL_BWD_FUSED_ATOMIC: the fp32 dQ accumulator, 4 * B * H * N_Q * d

@@ -216,3 +216,11 @@ def test_dispatch_size_limit(lib):
     st = lib.skl_forward_splitk(ctypes.byref(sk), *P, 0.1, 0.1, 0, 256, A, need, None)
     assert st == UNSUPPORTED
     assert "dispatch limit" in lib.skl_last_error().decode()
+
+
+def test_noalloc_rejects_partials_beyond_the_static_array(lib):
+    assert lib.skl_noalloc_scratch_bytes() == 32 << 20
+    s = _shape(B=1, H=64, NQ=4096, NK=8192)   # 20 * 64 * 4096 * 8 bytes = 40 MiB of partials
+    st = lib.skl_forward_splitk_noalloc(ctypes.byref(s), *P, 0.1, 0.1, 1, 8, A, A, A, None)
+    assert st == UNSUPPORTED
+    assert "static scratch" in lib.skl_last_error().decode()
