@@ -163,6 +163,41 @@ def kernel_alg_flops(w, wk, phase: str, algo: str):
     return {"bwd_fused_kernel": wk.student_flops if phase == "student" else wk.teacher_flops}
 
 
+def hbm_report(alg_bytes: int, traffic, ms: float):
+    """Per-kernel HBM figures: compulsory bytes and, with a counter figure for
+    the current source, the achieved GB/s (counter bytes / kernel time), its
+    fraction of the 8 TB/s peak and the counter/compulsory ratio."""
+    out = {"alg_bytes": int(alg_bytes), "hbm_bytes": traffic, "hbm_gbs": None, "hbm_frac": None,
+           "traffic_ratio": None}
+    if traffic:
+        from attention_kl_divergence_skl_amd import workmodel
+
+        gbs = traffic / (ms * 1e-3) / 1e9
+        out.update(hbm_gbs=gbs, hbm_frac=gbs / workmodel.PEAK_HBM_GBS, traffic_ratio=traffic / alg_bytes)
+    return out
+
+
+def kernel_alg_bytes(w, phase: str, algo: str):
+    """Compulsory HBM bytes of each main kernel of a phase: every input it
+    reads once, the per-row vectors it reads, and the outputs it writes once
+    (a workspace is an implementation cost and is not counted)."""
+    e = 2 if w.dtype == "bf16" else 4
+    BH = w.B * w.H
+    inputs = BH * (w.NQ + w.NK) * (w.d1 + w.d2) * e
+    rowvec = BH * w.NQ * 4
+    if phase == "fwd":
+        return {"fwd_kernel": inputs + 3 * rowvec}
+    if phase == "joint":
+        return {"bwd_joint_dk_kernel": inputs + 4 * rowvec + BH * w.NK * (w.d1 + w.d2) * e,
+                "bwd_joint_dq_kernel": inputs + 4 * rowvec + BH * w.NQ * (w.d1 + w.d2) * e}
+    dg = w.d2 if phase == "student" else w.d1
+    rv = (3 if phase == "student" else 4) * rowvec
+    if algo == "split":
+        return {"bwd_dk_kernel": inputs + rv + BH * w.NK * dg * e,
+                "bwd_dq_kernel": inputs + rv + BH * w.NQ * dg * e}
+    return {"bwd_fused_kernel": inputs + rv + BH * (w.NQ + w.NK) * dg * e}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -237,6 +272,7 @@ def main(argv=None) -> int:
     ws_s, ws_t = ws_for(False), ws_for(True)
     kflops = {p: kernel_flops(w, wk, p, algo) for p in phases}
     kalg = {p: kernel_alg_flops(w, wk, p, algo) for p in phases}
+    kbytes = {p: kernel_alg_bytes(w, p, algo) for p in phases}
     kev = {p: [] for p in phases}   # per call: events around its main kernels
     pev = {p: [] for p in phases}   # per call: events around the whole call
 
@@ -316,6 +352,9 @@ def main(argv=None) -> int:
             # alg_tflops / pct_peak_alg: its share of the algorithmic count.
             ks[name] = {"ms": kms, "tflops": tf, "pct_mfma_peak": 100.0 * tf / peak_tf,
                         "alg_tflops": atf, "pct_peak_alg": 100.0 * atf / peak_tf}
+            # HBM: compulsory bytes, and the calibrated counter bytes of the
+            # committed summary when it was taken on the current source.
+            ks[name].update(hbm_report(kbytes[p][name], kernel_traffic(name, p, traffic_key), kms))
             kernels.append((kms, p, name, kalg[p][name], fl))
         report[p] = {"call_ms": call_ms, "algorithmic_tflops": alg[p] / (call_ms * 1e-3) / 1e12,
                      "kernels": ks}
@@ -350,6 +389,8 @@ def main(argv=None) -> int:
             "unit": "TFLOP/s",
             "frac": ach / peak_tf,
             "traffic": kernel_traffic(dom_name, dom_phase, traffic_key),
+            **{k: v for k, v in report[dom_phase]["kernels"][dom_name].items()
+               if k in ("alg_bytes", "hbm_gbs", "traffic_ratio", "hbm_frac")},
             "flops_per_launch": dom_flops,
             "mfma_work_flops_per_launch": dom_mfma,
             "mfma_work_tflops": mfma_rate,

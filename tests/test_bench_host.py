@@ -57,3 +57,18 @@ def test_algorithmic_shares_sum_to_each_phase():
                 assert all(shares[k] <= own[k] for k in shares)
         joint = bench.kernel_alg_flops(w, wk, "joint", "joint")
         assert sum(joint.values()) == wk.student_flops + wk.teacher_flops
+
+
+def test_kernel_bytes_and_hbm_report():
+    w = synth.WORKLOADS["causal_64k_h32_d128_q1x4"]
+    wk = workmodel.work(w.B, w.H, w.NQ, w.NK, w.d1, w.d2, w.causal, 2)
+    assert bench.kernel_alg_bytes(w, "fwd", "split") == {"fwd_kernel": wk.fwd_bytes}
+    st = bench.kernel_alg_bytes(w, "student", "split")
+    # dK and dQ each read every input once and write their own gradient.
+    inputs = w.H * (w.NQ + w.NK) * (w.d1 + w.d2) * 2
+    assert st["bwd_dk_kernel"] == inputs + 3 * w.H * w.NQ * 4 + w.H * w.NK * w.d2 * 2
+    assert bench.kernel_alg_bytes(w, "student", "fused_atomic")["bwd_fused_kernel"] == wk.student_bytes
+    r = bench.hbm_report(2_000_000_000, 8_000_000_000, 10.0)
+    assert abs(r["hbm_gbs"] - 800.0) < 1e-9 and abs(r["traffic_ratio"] - 4.0) < 1e-12
+    assert abs(r["hbm_frac"] - 0.1) < 1e-12
+    assert bench.hbm_report(10, None, 1.0)["hbm_gbs"] is None
