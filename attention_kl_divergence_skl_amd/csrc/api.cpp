@@ -257,10 +257,10 @@ skl_status skl_forward(const skl_shape* s, const void* q1, const void* k1, const
   p.kl = kl;
   p.lse1 = lse1;
   p.lse2 = lse2;
-  return from_hip(timed(stream, [&] {
-                    return skl::launch_forward(p, s->dtype, s->d1, s->d2, causal != 0, false, s->B * s->H, stream);
-                  }),
-                  "skl_forward launch");
+  hipError_t e = mark(0, stream);
+  if (e == hipSuccess)
+    e = skl::launch_forward(p, s->dtype, s->d1, s->d2, causal != 0, false, s->B * s->H, stream, mark1);
+  return from_hip(e, "skl_forward launch");
 }
 
 size_t skl_forward_splitk_workspace_size(const skl_shape* s, int num_splits) {
@@ -283,10 +283,10 @@ skl_status skl_forward_splitk(const skl_shape* s, const void* q1, const void* k1
   p.splits = num_splits;
   p.split_len = (int32_t)split_len_for(s->NK, num_splits);
   p.part = static_cast<float*>(ws);
-  return from_hip(timed(stream, [&] {
-                    return skl::launch_forward(p, s->dtype, s->d1, s->d2, causal != 0, true, s->B * s->H, stream);
-                  }),
-                  "skl_forward_splitk launch");
+  hipError_t e = mark(0, stream);
+  if (e == hipSuccess)
+    e = skl::launch_forward(p, s->dtype, s->d1, s->d2, causal != 0, true, s->B * s->H, stream, mark1);
+  return from_hip(e, "skl_forward_splitk launch");
 }
 
 skl_status skl_reduce(const skl_shape* s, int num_splits, const void* ws, size_t ws_bytes, float* kl, float* lse1,

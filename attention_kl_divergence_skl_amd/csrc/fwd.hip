@@ -426,38 +426,43 @@ __global__ __launch_bounds__(256) void reduce_kernel(const ReduceParams p) {
 namespace {
 
 // The main pass, then the fixup pass over the same tiles (most of its
-// workgroups find no marked row and leave at once).
+// workgroups find no marked row and leave at once).  `between` runs after the
+// main pass's launch (profiling events).
 template <typename T, int D1, int D2, bool C, bool S>
-hipError_t run_fwd(const FwdParams& p, int64_t BH, hipStream_t s) {
+hipError_t run_fwd(const FwdParams& p, int64_t BH, hipStream_t s, void (*between)(hipStream_t)) {
   const int64_t grid = BH * p.num_qtiles * (S ? p.splits : 1);
   hipLaunchKernelGGL((fwd_kernel<T, D1, D2, C, S, false>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (between) between(s);
   hipLaunchKernelGGL((fwd_kernel<T, D1, D2, C, S, true>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
 template <typename T, int D1, int D2>
-hipError_t fwd_dims(const FwdParams& p, bool causal, bool split, int64_t BH, hipStream_t s) {
-  if (causal) return split ? run_fwd<T, D1, D2, true, true>(p, BH, s) : run_fwd<T, D1, D2, true, false>(p, BH, s);
-  return split ? run_fwd<T, D1, D2, false, true>(p, BH, s) : run_fwd<T, D1, D2, false, false>(p, BH, s);
+hipError_t fwd_dims(const FwdParams& p, bool causal, bool split, int64_t BH, hipStream_t s,
+                    void (*bw)(hipStream_t)) {
+  if (causal)
+    return split ? run_fwd<T, D1, D2, true, true>(p, BH, s, bw) : run_fwd<T, D1, D2, true, false>(p, BH, s, bw);
+  return split ? run_fwd<T, D1, D2, false, true>(p, BH, s, bw) : run_fwd<T, D1, D2, false, false>(p, BH, s, bw);
 }
 
 template <typename T>
-hipError_t fwd_type(const FwdParams& p, int d1, int d2, bool causal, bool split, int64_t BH, hipStream_t s) {
-  if (d1 == 128 && d2 == 128) return fwd_dims<T, 128, 128>(p, causal, split, BH, s);
-  if (d1 == 128 && d2 == 64) return fwd_dims<T, 128, 64>(p, causal, split, BH, s);
-  if (d1 == 64 && d2 == 128) return fwd_dims<T, 64, 128>(p, causal, split, BH, s);
-  if (d1 == 64 && d2 == 64) return fwd_dims<T, 64, 64>(p, causal, split, BH, s);
+hipError_t fwd_type(const FwdParams& p, int d1, int d2, bool causal, bool split, int64_t BH, hipStream_t s,
+                    void (*bw)(hipStream_t)) {
+  if (d1 == 128 && d2 == 128) return fwd_dims<T, 128, 128>(p, causal, split, BH, s, bw);
+  if (d1 == 128 && d2 == 64) return fwd_dims<T, 128, 64>(p, causal, split, BH, s, bw);
+  if (d1 == 64 && d2 == 128) return fwd_dims<T, 64, 128>(p, causal, split, BH, s, bw);
+  if (d1 == 64 && d2 == 64) return fwd_dims<T, 64, 64>(p, causal, split, BH, s, bw);
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_forward(const FwdParams& p, int dtype, int d1, int d2, bool causal, bool split,
-                          int64_t BH, hipStream_t s) {
-  if (dtype == 0) return fwd_type<bf16>(p, d1, d2, causal, split, BH, s);
-  return fwd_type<float>(p, d1, d2, causal, split, BH, s);
+                          int64_t BH, hipStream_t s, void (*between)(hipStream_t)) {
+  if (dtype == 0) return fwd_type<bf16>(p, d1, d2, causal, split, BH, s, between);
+  return fwd_type<float>(p, d1, d2, causal, split, BH, s, between);
 }
 
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s) {

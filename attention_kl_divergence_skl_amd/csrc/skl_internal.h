@@ -96,8 +96,11 @@ struct ConvertParams {
 };
 
 // Launchers: return the result of hipGetLastError() after the launch.
+// Forward: the main pass, then the fixup pass that recomputes only the
+// tiles the main pass marked.  `between` runs after the main pass's launch
+// (profiling events).
 hipError_t launch_forward(const FwdParams& p, int dtype, int d1, int d2, bool causal, bool split,
-                          int64_t BH, hipStream_t s);
+                          int64_t BH, hipStream_t s, void (*between)(hipStream_t));
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s);
 hipError_t launch_zero(float* ws, int64_t count, hipStream_t s);
 // Fused backward: one kernel, dQ through fp32 atomics into p.ws.

@@ -249,9 +249,11 @@ int skl_recommended_splits(const skl_shape* shape, int causal, int num_cus);
  * records events[0] on its stream right before enqueueing its first main
  * kernel and events[k] right after its k-th main kernel (k < count), so
  * hipEventElapsedTime(events[k-1], events[k]) is the k-th kernel's duration.
- * Main kernels: the forward or split-K forward kernel (one); the split
- * backward's dK kernel then dQ kernel (two); the fused backward kernel
- * (one).  Workspace clears, the reduce and the dQ convert are not counted.
+ * Main kernels: the forward or split-K forward kernel's main pass (one; its
+ * fixup pass, which recomputes only the tiles the main pass marked, is not
+ * counted); the split backward's dK kernel then dQ kernel (two); the fused
+ * backward kernel (one).  Workspace clears, the reduce and the dQ convert are
+ * not counted.
  * count = 0 switches it off; at most 4 events.  The events stay owned by the
  * caller.
  */

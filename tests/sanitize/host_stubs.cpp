@@ -34,11 +34,13 @@ const char* hipGetErrorString(hipError_t) { return "stubbed HIP error"; }
 
 namespace skl {
 
-hipError_t launch_forward(const FwdParams& p, int, int, int, bool, bool split, int64_t BH, hipStream_t) {
+hipError_t launch_forward(const FwdParams& p, int, int, int, bool, bool split, int64_t BH, hipStream_t s,
+                          void (*between)(hipStream_t)) {
   ++stub::log.forward;
   stub::log.fwd = p;
   stub::log.fwd_split = split;
   stub::log.BH = BH;
+  if (between) between(s);
   return hipSuccess;
 }
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t) {
