@@ -396,8 +396,9 @@ def skl_recommended_splits(q1, k1, q2, k2, causal: bool = False, num_cus: Option
 # does not depend on (Q2, K2) and P2 does not depend on (Q1, K1), so the
 # student call ("optimise P2") gives exactly dKL/d(Q2, K2) and the teacher
 # call ("optimise P1") exactly dKL/d(Q1, K1); backward launches only the
-# settings whose inputs require a gradient (a frozen teacher costs one; both
-# at once use the joint kernels).
+# settings whose inputs require a gradient (a frozen teacher costs one).  When
+# both do, the two split calls run one after the other: on MI355X they are
+# faster than the joint kernels (algo="joint" selects those).
 # ---------------------------------------------------------------------------
 
 def _autograd_function():
@@ -424,9 +425,12 @@ def _autograd_function():
             dq1 = dk1 = dq2 = dk2 = None
             need_s = ctx.needs_input_grad[2] or ctx.needs_input_grad[3]
             need_t = ctx.needs_input_grad[0] or ctx.needs_input_grad[1]
-            if need_s and need_t and algo == "split":
-                dq1, dk1, dq2, dk2 = skl_backward_joint(q1, k1, q2, k2, lse1, lse2, kl, g, scale1, scale2, causal)
-                return dq1, dk1, dq2, dk2, None, None, None, None
+            if algo == "joint":
+                if need_s and need_t:
+                    dq1, dk1, dq2, dk2 = skl_backward_joint(q1, k1, q2, k2, lse1, lse2, kl, g, scale1, scale2,
+                                                            causal)
+                    return dq1, dk1, dq2, dk2, None, None, None, None
+                algo = "split"
             if need_s:
                 dq2, dk2 = skl_backward_student(q1, k1, q2, k2, lse1, lse2, g, scale1, scale2, causal, algo=algo)
             if need_t:
@@ -445,7 +449,9 @@ def attention_kl(q1, k1, q2, k2, scale1=None, scale2=None, causal: bool = False,
 
     Returns (kl, lse1, lse2); kl [B, H, N_Q] fp32 carries gradients to every
     input that requires one (the LSEs are auxiliary and not differentiable).
-    Scales default to 1/sqrt(d_k)."""
+    Scales default to 1/sqrt(d_k).  algo: "split" (default; the measured
+    fastest), "fused_atomic", or "joint" (both settings from one recompute
+    when all four inputs need gradients)."""
     global _ATTENTION_KL
     if _ATTENTION_KL is None:
         _ATTENTION_KL = _autograd_function()

@@ -17,15 +17,16 @@ def W(name, B, H, NQ, NK, d1, d2, dtype, causal, recipe=synth.Recipe("corr", noi
                           recipe, "random", 3)
 
 
+@pytest.mark.parametrize("algo", ["split", "joint"])
 @pytest.mark.parametrize("w", [W("ag_bf16_causal", 1, 2, 300, 300, 128, 128, "bf16", True),
                                W("ag_f32_noncausal", 2, 1, 130, 200, 64, 128, "f32", False, synth.Recipe("iid"))],
                          ids=lambda w: w.name)
-def test_autograd_gradients_of_all_inputs(gpu_lib, w):
-    say(f"[autograd] {w.name}")
+def test_autograd_gradients_of_all_inputs(gpu_lib, w, algo):
+    say(f"[autograd {algo}] {w.name}")
     x, t = to_device(w)
     leaves = {k: t[k].clone().requires_grad_(True) for k in ("q1", "k1", "q2", "k2")}
     kl, lse1, lse2 = gpu_lib.attention_kl(leaves["q1"], leaves["k1"], leaves["q2"], leaves["k2"],
-                                          w.scale1, w.scale2, w.causal)
+                                          w.scale1, w.scale2, w.causal, algo=algo)
     assert not lse1.requires_grad and not lse2.requires_grad
     (kl * t["g"]).sum().backward()
     torch.cuda.synchronize()
