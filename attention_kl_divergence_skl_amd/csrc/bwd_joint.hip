@@ -65,13 +65,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_joint_dk_kernel(const BwdPara
   using T1 = SwzTile<RB1>;
   using T2 = SwzTile<RB2>;
 
-  __shared__ __attribute__((aligned(1024))) char sQ1[2][BQ * RB1];
-  __shared__ __attribute__((aligned(1024))) char sQ2[2][BQ * RB2];
-  __shared__ __attribute__((aligned(16))) float sVec[2][4][BQ];  // L1, L2 (base 2), g, g KL
+  // Ring stages as separate LDS variables, so that the compiler can tell
+  // reads of one stage from the direct-to-LDS loads in flight into the other.
+  __shared__ __attribute__((aligned(1024))) char sQ1a[BQ * RB1], sQ1b[BQ * RB1];
+  __shared__ __attribute__((aligned(1024))) char sQ2a[BQ * RB2], sQ2b[BQ * RB2];
+  __shared__ __attribute__((aligned(16))) float sVa[4][BQ], sVb[4][BQ];  // L1, L2 (base 2), g, g KL
+  auto sQ1 = [&](int st) __attribute__((always_inline)) -> char* { return st ? sQ1b : sQ1a; };
+  auto sQ2 = [&](int st) __attribute__((always_inline)) -> char* { return st ? sQ2b : sQ2a; };
+  auto sVec = [&](int st) __attribute__((always_inline)) -> float(*)[BQ] { return st ? sVb : sVa; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int half = lane >> 5, col = lane & 31;
 
   const int64_t t = xcd_remap(blockIdx.x, gridDim.x);
@@ -117,8 +122,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_joint_dk_kernel(const BwdPara
   const float* const vsrc = which == 0 ? p.lse1 : which == 1 ? p.lse2 : p.dkl;
   float pv = 0.f, pv2 = 0.f;
   auto fetch = [&](int st, int64_t q0) {
-    tile_load_async<BQ, RB1>(sQ1[st], q1p, p.sq1.n * ESZ, (int)q0, (int)p.NQ, wave, lane);
-    tile_load_async<BQ, RB2>(sQ2[st], q2p, p.sq2.n * ESZ, (int)q0, (int)p.NQ, wave, lane);
+    tile_load_async<BQ, RB1>(sQ1(st), q1p, p.sq1.n * ESZ, (int)q0, (int)p.NQ, wave, lane);
+    tile_load_async<BQ, RB2>(sQ2(st), q2p, p.sq2.n * ESZ, (int)q0, (int)p.NQ, wave, lane);
     const int64_t q = q0 + vrow;
     const int64_t o = bh * p.NQ + (q < p.NQ ? q : p.NQ - 1);  // rows past N_Q are zeroed at the stash
     pv = vsrc[o];
@@ -126,7 +131,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_joint_dk_kernel(const BwdPara
   };
   auto stash = [&](int st, int64_t q0) {
     const float v = which == 3 ? pv * pv2 : which == 2 ? pv : pv * kLog2e;  // L1, L2 (base 2), g, g KL
-    sVec[st][which][vrow] = (q0 + vrow < p.NQ) ? v : 0.f;
+    sVec(st)[which][vrow] = (q0 + vrow < p.NQ) ? v : 0.f;
   };
 
   if (nsteps > 0) {
@@ -140,14 +145,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_joint_dk_kernel(const BwdPara
   const SwzAddr<RB1> ad1(prow, half, lane);
   const SwzAddr<RB2> ad2(prow, half, lane);
 
-  auto step = [&](auto masked, int64_t it) __attribute__((always_inline)) {
-    const int st = (int)(it & 1);
+  // One query step; the stage is a compile-time constant in the mask-free
+  // steps (run in pairs), so it folds into the immediate offset of every
+  // LDS read.
+  auto step = [&](auto masked, auto stc, int64_t it) __attribute__((always_inline)) {
+    const int st = stc;  // it & 1
     constexpr bool MASKED = decltype(masked)::value;
     const int64_t q0 = qbeg + it * BQ;
     if (it + 1 < nsteps) fetch(st ^ 1, q0 + BQ);
-
-    const SwzAddr<RB1> x1 = ad1.shifted(st * BQ * RB1);
-    const SwzAddr<RB2> x2 = ad2.shifted(st * BQ * RB2);
+    const char* const tq1 = sQ1(st);
+    const char* const tq2 = sQ2(st);
 #pragma unroll
     for (int qb = 0; qb < BQ / 32; ++qb) {
       const int64_t qb0 = q0 + 32 * qb;
@@ -157,15 +164,23 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_joint_dk_kernel(const BwdPara
         const int qrow = 32 * qb + prow;
 #pragma unroll
         for (int c = 0; c < NC1; ++c)
-          s1 = M::run(M::load(&sQ1[st][T1::off(qrow, (c * KC + half * EPL) * ESZ)]), kf1[c], s1);
+          s1 = M::run(M::load(&tq1[T1::off(qrow, (c * KC + half * EPL) * ESZ)]), kf1[c], s1);
 #pragma unroll
         for (int c = 0; c < NC2; ++c)
-          s2 = M::run(M::load(&sQ2[st][T2::off(qrow, (c * KC + half * EPL) * ESZ)]), kf2[c], s2);
+          s2 = M::run(M::load(&tq2[T2::off(qrow, (c * KC + half * EPL) * ESZ)]), kf2[c], s2);
       } else {
+        // All operand fragments of the block are read before its MFMA chains
+        // (one wave per SIMD: no other wave hides the LDS latency).
+        frag pa1[NC1], pa2[NC2];
 #pragma unroll
-        for (int c = 0; c < NC1; ++c) s1 = M::run(x1.frag(sQ1[0], 32 * qb * RB1, c), kf1[c], s1);
+        for (int c = 0; c < NC1; ++c) pa1[c] = ad1.frag(tq1, 32 * qb * RB1, c);
 #pragma unroll
-        for (int c = 0; c < NC2; ++c) s2 = M::run(x2.frag(sQ2[0], 32 * qb * RB2, c), kf2[c], s2);
+        for (int c = 0; c < NC2; ++c) pa2[c] = ad2.frag(tq2, 32 * qb * RB2, c);
+#pragma unroll
+        for (int c = 0; c < (NC1 > NC2 ? NC1 : NC2); ++c) {
+          if (c < NC1) s1 = M::run(pa1[c], kf1[c], s1);
+          if (c < NC2) s2 = M::run(pa2[c], kf2[c], s2);
+        }
       }
 
       // Registers 8 run .. 8 run + 7 hold rows 32 qb + 16 run + 8 half + 0..7
@@ -175,10 +190,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_joint_dk_kernel(const BwdPara
       const int qlim = clamp_i32(p.NQ - qb0), cmin = clamp_i32(key - qb0 - off);
 #pragma unroll
       for (int run = 0; run < 2; ++run) {
+        // Gradient operands read before the dS work, so their latency
+        // overlaps it.
+        frag bq1[NB1], bq2[NB2];
+        if constexpr (EPL != 1) {
+#pragma unroll
+          for (int cb = 0; cb < NB1; ++cb) bq1[cb] = ad1.trfrag(tq1, (32 * qb + run * KC) * RB1, cb);
+#pragma unroll
+          for (int cb = 0; cb < NB2; ++cb) bq2[cb] = ad2.trfrag(tq2, (32 * qb + run * KC) * RB2, cb);
+        }
         float cst[4][8];
 #pragma unroll
         for (int which = 0; which < 4; ++which) {
-          const float4* v = reinterpret_cast<const float4*>(&sVec[st][which][32 * qb + 16 * run + 8 * half]);
+          const float4* v = reinterpret_cast<const float4*>(&sVec(st)[which][32 * qb + 16 * run + 8 * half]);
           const float4 y0 = v[0], y1 = v[1];
           cst[which][0] = y0.x; cst[which][1] = y0.y; cst[which][2] = y0.z; cst[which][3] = y0.w;
           cst[which][4] = y1.x; cst[which][5] = y1.y; cst[which][6] = y1.z; cst[which][7] = y1.w;
@@ -206,11 +230,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_joint_dk_kernel(const BwdPara
             const int qr = 32 * qb + rloc(c, half);
 #pragma unroll
             for (int cb = 0; cb < NB1; ++cb)
-              dk1[cb] = M::run(ds1[i], *reinterpret_cast<const float*>(&sQ1[st][T1::off(qr, (32 * cb + col) * ESZ)]),
+              dk1[cb] = M::run(ds1[i], *reinterpret_cast<const float*>(&tq1[T1::off(qr, (32 * cb + col) * ESZ)]),
                                dk1[cb]);
 #pragma unroll
             for (int cb = 0; cb < NB2; ++cb)
-              dk2[cb] = M::run(ds2[i], *reinterpret_cast<const float*>(&sQ2[st][T2::off(qr, (32 * cb + col) * ESZ)]),
+              dk2[cb] = M::run(ds2[i], *reinterpret_cast<const float*>(&tq2[T2::off(qr, (32 * cb + col) * ESZ)]),
                                dk2[cb]);
           }
         } else {
@@ -221,9 +245,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_joint_dk_kernel(const BwdPara
             a2[e] = from_f32<T>(ds2[e]);
           }
 #pragma unroll
-          for (int cb = 0; cb < NB1; ++cb) dk1[cb] = M::run(a1, x1.trfrag(sQ1[0], (32 * qb + run * KC) * RB1, cb), dk1[cb]);
+          for (int cb = 0; cb < NB1; ++cb) dk1[cb] = M::run(a1, bq1[cb], dk1[cb]);
 #pragma unroll
-          for (int cb = 0; cb < NB2; ++cb) dk2[cb] = M::run(a2, x2.trfrag(sQ2[0], (32 * qb + run * KC) * RB2, cb), dk2[cb]);
+          for (int cb = 0; cb < NB2; ++cb) dk2[cb] = M::run(a2, bq2[cb], dk2[cb]);
         }
       }
     }
@@ -241,10 +265,23 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_joint_dk_kernel(const BwdPara
     if (CAUSAL && x > 0) head = min(nsteps, (x + BQ - 1) / BQ);
     if (p.NQ % BQ != 0) tail = max(head, nsteps - 1);
   }
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
   int64_t it = 0;
-  for (; it < head; ++it) step(std::true_type{}, it);
-  for (; it < tail; ++it) step(std::false_type{}, it);
-  for (; it < nsteps; ++it) step(std::true_type{}, it);
+  for (; it < head; ++it) step(std::true_type{}, (int)(it & 1), it);
+  if constexpr (EPL != 1) {
+    // (fp32 keeps one step per iteration: the unrolled pair spills there.)
+    if (it < tail && (it & 1)) {
+      step(std::false_type{}, I1{}, it);
+      ++it;
+    }
+    for (; it + 1 < tail; it += 2) {
+      step(std::false_type{}, I0{}, it);
+      step(std::false_type{}, I1{}, it + 1);
+    }
+  }
+  for (; it < tail; ++it) step(std::false_type{}, (int)(it & 1), it);
+  for (; it < nsteps; ++it) step(std::true_type{}, (int)(it & 1), it);
 
   char* const dk1p = (char*)p.dk + (b * p.sdk.b + h * p.sdk.h) * ESZ;
   char* const dk2p = (char*)p.dk_s + (b * p.sdk_s.b + h * p.sdk_s.h) * ESZ;
@@ -281,12 +318,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_joint_dq_kernel(const BwdPara
   using T1 = SwzTile<RB1>;
   using T2 = SwzTile<RB2>;
 
-  __shared__ __attribute__((aligned(1024))) char sK1[2][BK * RB1];
-  __shared__ __attribute__((aligned(1024))) char sK2[2][BK * RB2];
+  __shared__ __attribute__((aligned(1024))) char sK1a[BK * RB1], sK1b[BK * RB1];
+  __shared__ __attribute__((aligned(1024))) char sK2a[BK * RB2], sK2b[BK * RB2];
+  auto sK1 = [&](int st) __attribute__((always_inline)) -> char* { return st ? sK1b : sK1a; };
+  auto sK2 = [&](int st) __attribute__((always_inline)) -> char* { return st ? sK2b : sK2a; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int half = lane >> 5, col = lane & 31;
 
   const int num_qtiles = (int)((p.NQ + BQ - 1) / BQ);
@@ -335,8 +374,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_joint_dq_kernel(const BwdPara
   const int64_t wave_kmax = CAUSAL ? qw0 + 31 + off : p.NK - 1;
 
   auto fetch = [&](int st, int64_t j0) {
-    tile_load_async<BK, RB1>(sK1[st], k1p, p.sk1.n * ESZ, (int)j0, (int)p.NK, wave, lane);
-    tile_load_async<BK, RB2>(sK2[st], k2p, p.sk2.n * ESZ, (int)j0, (int)p.NK, wave, lane);
+    tile_load_async<BK, RB1>(sK1(st), k1p, p.sk1.n * ESZ, (int)j0, (int)p.NK, wave, lane);
+    tile_load_async<BK, RB2>(sK2(st), k2p, p.sk2.n * ESZ, (int)j0, (int)p.NK, wave, lane);
   };
 
   if (nsteps > 0) fetch(0, 0);
@@ -345,11 +384,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_joint_dq_kernel(const BwdPara
   const float c1 = p.c1, c2 = p.c2;
   const int prow = rperm(col);
 
-  auto step = [&](auto masked, int64_t it) __attribute__((always_inline)) {
+  auto step = [&](auto masked, auto stc, int64_t it) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked)::value;
-    const int st = (int)(it & 1);
+    const int st = stc;  // it & 1; a compile-time constant in the mask-free steps
     const int64_t j0 = it * BK;
     if (it + 1 < nsteps) fetch(st ^ 1, j0 + BK);
+    const char* const tk1 = sK1(st);
+    const char* const tk2 = sK2(st);
 
     if (!MASKED || wave_uniform(j0 <= wave_kmax)) {
       const bool need_mask =
@@ -359,15 +400,38 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_joint_dq_kernel(const BwdPara
         f32x16 s1 = f32x16{}, s2 = f32x16{};
         const int klim = clamp_i32(p.NK - (j0 + kb * 32)), cmax = clamp_i32(qi + off - (j0 + kb * 32));
         const int krow = kb * 32 + prow;
+        // All operand fragments of the block are read before its MFMA chains
+        // (one wave per SIMD: no other wave hides the LDS latency).
+        if constexpr (EPL != 1) {
+          frag ka1[NC1], ka2[NC2];
 #pragma unroll
-        for (int c = 0; c < NC1; ++c)
-          s1 = M::run(M::load(&sK1[st][T1::off(krow, (c * KC + half * EPL) * ESZ)]), qf1[c], s1);
+          for (int c = 0; c < NC1; ++c) ka1[c] = M::load(&tk1[T1::off(krow, (c * KC + half * EPL) * ESZ)]);
 #pragma unroll
-        for (int c = 0; c < NC2; ++c)
-          s2 = M::run(M::load(&sK2[st][T2::off(krow, (c * KC + half * EPL) * ESZ)]), qf2[c], s2);
+          for (int c = 0; c < NC2; ++c) ka2[c] = M::load(&tk2[T2::off(krow, (c * KC + half * EPL) * ESZ)]);
+#pragma unroll
+          for (int c = 0; c < (NC1 > NC2 ? NC1 : NC2); ++c) {
+            if (c < NC1) s1 = M::run(ka1[c], qf1[c], s1);
+            if (c < NC2) s2 = M::run(ka2[c], qf2[c], s2);
+          }
+        } else {
+#pragma unroll
+          for (int c = 0; c < NC1; ++c)
+            s1 = M::run(M::load(&tk1[T1::off(krow, (c * KC + half * EPL) * ESZ)]), qf1[c], s1);
+#pragma unroll
+          for (int c = 0; c < NC2; ++c)
+            s2 = M::run(M::load(&tk2[T2::off(krow, (c * KC + half * EPL) * ESZ)]), qf2[c], s2);
+        }
         // Registers 8 run .. 8 run + 7 hold keys kb 32 + 16 run + 8 half + 0..7.
 #pragma unroll
         for (int run = 0; run < 2; ++run) {
+          // Gradient operands read before the dS work.
+          frag bk1[NB1], bk2[NB2];
+          if constexpr (EPL != 1) {
+#pragma unroll
+            for (int cb = 0; cb < NB1; ++cb) bk1[cb] = lds_tr_frag_swz<RB1>(tk1, kb * 32 + run * KC, 32 * cb, lane);
+#pragma unroll
+            for (int cb = 0; cb < NB2; ++cb) bk2[cb] = lds_tr_frag_swz<RB2>(tk2, kb * 32 + run * KC, 32 * cb, lane);
+          }
           float ds1[8], ds2[8];
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
@@ -389,11 +453,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_joint_dq_kernel(const BwdPara
               const int kr = kb * 32 + rloc(8 * run + i, half);
 #pragma unroll
               for (int cb = 0; cb < NB1; ++cb)
-                dq1[cb] = M::run(ds1[i], *reinterpret_cast<const float*>(&sK1[st][T1::off(kr, (32 * cb + col) * ESZ)]),
+                dq1[cb] = M::run(ds1[i], *reinterpret_cast<const float*>(&tk1[T1::off(kr, (32 * cb + col) * ESZ)]),
                                  dq1[cb]);
 #pragma unroll
               for (int cb = 0; cb < NB2; ++cb)
-                dq2[cb] = M::run(ds2[i], *reinterpret_cast<const float*>(&sK2[st][T2::off(kr, (32 * cb + col) * ESZ)]),
+                dq2[cb] = M::run(ds2[i], *reinterpret_cast<const float*>(&tk2[T2::off(kr, (32 * cb + col) * ESZ)]),
                                  dq2[cb]);
             }
           } else {
@@ -405,10 +469,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_joint_dq_kernel(const BwdPara
             }
 #pragma unroll
             for (int cb = 0; cb < NB1; ++cb)
-              dq1[cb] = M::run(a1, lds_tr_frag_swz<RB1>(&sK1[st][0], kb * 32 + run * KC, 32 * cb, lane), dq1[cb]);
+              dq1[cb] = M::run(a1, bk1[cb], dq1[cb]);
 #pragma unroll
-            for (int cb = 0; cb < NB2; ++cb)
-              dq2[cb] = M::run(a2, lds_tr_frag_swz<RB2>(&sK2[st][0], kb * 32 + run * KC, 32 * cb, lane), dq2[cb]);
+            for (int cb = 0; cb < NB2; ++cb) dq2[cb] = M::run(a2, bk2[cb], dq2[cb]);
           }
         }
       }
@@ -424,9 +487,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_joint_dq_kernel(const BwdPara
     tail = min(nsteps, first_ge(p.NK - BK + 1));
     if (CAUSAL) tail = min(tail, first_ge((int64_t)qt * BQ + off - BK + 2));
   }
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
   int64_t it = 0;
-  for (; it < tail; ++it) step(std::false_type{}, it);
-  for (; it < nsteps; ++it) step(std::true_type{}, it);
+  if constexpr (EPL != 1) {
+    // (fp32 keeps one step per iteration: the unrolled pair spills there.)
+    for (; it + 1 < tail; it += 2) {
+      step(std::false_type{}, I0{}, it);
+      step(std::false_type{}, I1{}, it + 1);
+    }
+  }
+  for (; it < tail; ++it) step(std::false_type{}, (int)(it & 1), it);
+  for (; it < nsteps; ++it) step(std::true_type{}, (int)(it & 1), it);
 
   char* const dq1p = (char*)p.dq + (b * p.sdq.b + h * p.sdq.h) * ESZ;
   char* const dq2p = (char*)p.dq_s + (b * p.sdq_s.b + h * p.sdq_s.h) * ESZ;
