@@ -32,15 +32,33 @@ namespace skl {
 
 namespace {
 
-// Both dS values of one accumulator element from the raw logits and the row
-// constants L_k = LSE_k log2 e, g, gl = g ln2 and gk = g KL.
-__device__ __forceinline__ void dS_both(float s1, float s2, float c1, float c2, float L1, float L2, float g,
-                                        float gl, float gk, float& ds1, float& ds2) {
-  const float u1 = fmaf(s1, c1, -L1);
-  const float u2 = fmaf(s2, c2, -L2);
-  const float p1 = exp2_hw(u1), p2 = exp2_hw(u2);
-  ds2 = g * (p2 - p1);
-  ds1 = p1 * fmaf(gl, u1 - u2, -gk);
+// |g| goes into the exponents: with k = log2 |g| and the row constants
+// A_k = LSE_k log2 e - k, w_k = t_k - A_k gives 2^w_k = |g| P_k, and
+//   sign(g) dS2 = 2^w2 - 2^w1,   sign(g) dS1 = 2^w1 (ln2 (w1 - w2) - KL)
+// (k cancels in w1 - w2).  Six vector ops and two exponentials per element;
+// the sign of g multiplies the finished dQ rows, and dS only in the rare dK
+// tiles that have a row with g < 0.  A row with g = 0 gets A1 = A2 = kZeroRow:
+// both exponentials are 0 and w1 - w2 = 0, so both dS are exactly 0.
+constexpr float kZeroRow = 1e30f;
+
+__device__ __forceinline__ void joint_row_consts(float lse1, float lse2, float g, float& A1, float& A2) {
+  if (g == 0.f) {
+    A1 = kZeroRow;
+    A2 = kZeroRow;
+    return;
+  }
+  const float k = log2f(fabsf(g));
+  A1 = fmaf(lse1, kLog2e, -k);
+  A2 = fmaf(lse2, kLog2e, -k);
+}
+
+__device__ __forceinline__ void dS_both_abs(float s1, float s2, float c1, float c2, float A1, float A2, float kl,
+                                            float& ds1, float& ds2) {
+  const float w1 = fmaf(s1, c1, -A1);
+  const float w2 = fmaf(s2, c2, -A2);
+  const float e1 = exp2_hw(w1), e2 = exp2_hw(w2);
+  ds2 = e2 - e1;
+  ds1 = e1 * fmaf(w1 - w2, kLn2, -kl);
 }
 
 }  // namespace
@@ -49,8 +67,8 @@ __device__ __forceinline__ void dS_both(float s1, float s2, float c1, float c2, 
 // Joint dK kernel: 4 waves own 128 keys (32 each) of one (b, h) and walk the
 // query tiles of 64 rows that see them, 32 rows at a time.  K fragments of
 // both sides stay in registers; Q1/Q2 tiles come straight into a
-// double-buffered swizzled LDS ring with the row constants (L1, L2, g, g KL)
-// beside them.
+// double-buffered swizzled LDS ring with the row constants (A1, A2, KL and
+// the sign of g) beside them.
 // ---------------------------------------------------------------------------
 template <typename T, int D1, int D2, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void bwd_joint_dk_kernel(const BwdParams p) {
@@ -69,7 +87,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_joint_dk_kernel(const BwdPara
   // reads of one stage from the direct-to-LDS loads in flight into the other.
   __shared__ __attribute__((aligned(1024))) char sQ1a[BQ * RB1], sQ1b[BQ * RB1];
   __shared__ __attribute__((aligned(1024))) char sQ2a[BQ * RB2], sQ2b[BQ * RB2];
-  __shared__ __attribute__((aligned(16))) float sVa[4][BQ], sVb[4][BQ];  // L1, L2 (base 2), g, g KL
+  // Per query row of a tile: A1, A2, KL and sign(g); plus a flag per stage:
+  // some row of the tile has g < 0.
+  __shared__ __attribute__((aligned(16))) float sVa[4][BQ], sVb[4][BQ];
+  __shared__ int sNeg[2];
   auto sQ1 = [&](int st) __attribute__((always_inline)) -> char* { return st ? sQ1b : sQ1a; };
   auto sQ2 = [&](int st) __attribute__((always_inline)) -> char* { return st ? sQ2b : sQ2a; };
   auto sVec = [&](int st) __attribute__((always_inline)) -> float(*)[BQ] { return st ? sVb : sVa; };
@@ -112,26 +133,38 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_joint_dk_kernel(const BwdPara
   if (CAUSAL) qbeg = max((int64_t)0, kt0 - off) / BQ * BQ;
   const int64_t nsteps = (p.NQ - qbeg + BQ - 1) / BQ;
 
-  // Row constants of the next query tile (wave w holds constant w of its 64
-  // rows): the fetch only loads them and the stash, after the step's
-  // compute, scales them, so no wave waits for the next tile's loads
-  // mid-step (any arithmetic on a loaded value makes it wait for all of its
-  // outstanding loads).
-  static_assert(4 * BQ == kThreads, "one wave per row constant");
-  const int which = tid / BQ, vrow = tid % BQ;  // which == wave
-  const float* const vsrc = which == 0 ? p.lse1 : which == 1 ? p.lse2 : p.dkl;
-  float pv = 0.f, pv2 = 0.f;
+  // Row values of the next query tile (LSE1, LSE2, g, KL) are loaded by the
+  // first wave, one row per lane; the fetch only loads them and the stash,
+  // after the step's compute, forms the row constants, so no wave waits for
+  // the next tile's loads mid-step (any arithmetic on a loaded value makes it
+  // wait for all of its outstanding loads).
+  static_assert(BQ == 64, "one lane of the first wave per query row");
+  float pl1 = 0.f, pl2 = 0.f, pg = 0.f, pkl = 0.f;
   auto fetch = [&](int st, int64_t q0) {
     tile_load_async<BQ, RB1>(sQ1(st), q1p, p.sq1.n * ESZ, (int)q0, (int)p.NQ, wave, lane);
     tile_load_async<BQ, RB2>(sQ2(st), q2p, p.sq2.n * ESZ, (int)q0, (int)p.NQ, wave, lane);
-    const int64_t q = q0 + vrow;
-    const int64_t o = bh * p.NQ + (q < p.NQ ? q : p.NQ - 1);  // rows past N_Q are zeroed at the stash
-    pv = vsrc[o];
-    if (which == 3) pv2 = p.kl[o];
+    if (wave == 0) {
+      const int64_t q = q0 + lane;
+      const int64_t o = bh * p.NQ + (q < p.NQ ? q : p.NQ - 1);  // rows past N_Q are zeroed at the stash
+      pl1 = p.lse1[o];
+      pl2 = p.lse2[o];
+      pg = p.dkl[o];
+      pkl = p.kl[o];
+    }
   };
   auto stash = [&](int st, int64_t q0) {
-    const float v = which == 3 ? pv * pv2 : which == 2 ? pv : pv * kLog2e;  // L1, L2 (base 2), g, g KL
-    sVec(st)[which][vrow] = (q0 + vrow < p.NQ) ? v : 0.f;
+    if (wave == 0) {
+      const bool valid = q0 + lane < p.NQ;
+      float A1 = kZeroRow, A2 = kZeroRow;
+      if (valid) joint_row_consts(pl1, pl2, pg, A1, A2);
+      float(*v)[BQ] = sVec(st);
+      v[0][lane] = A1;
+      v[1][lane] = A2;
+      v[2][lane] = valid ? pkl : 0.f;
+      v[3][lane] = (valid && pg < 0.f) ? -1.f : 1.f;
+      const bool neg = __builtin_amdgcn_ballot_w64(valid && pg < 0.f) != 0;
+      if (lane == 0) sNeg[st] = neg ? 1 : 0;
+    }
   };
 
   if (nsteps > 0) {
@@ -155,6 +188,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_joint_dk_kernel(const BwdPara
     if (it + 1 < nsteps) fetch(st ^ 1, q0 + BQ);
     const char* const tq1 = sQ1(st);
     const char* const tq2 = sQ2(st);
+    const bool neg_tile = __builtin_amdgcn_readfirstlane(sNeg[st]) != 0;
 #pragma unroll
     for (int qb = 0; qb < BQ / 32; ++qb) {
       const int64_t qb0 = q0 + 32 * qb;
@@ -199,20 +233,30 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_joint_dk_kernel(const BwdPara
 #pragma unroll
           for (int cb = 0; cb < NB2; ++cb) bq2[cb] = ad2.trfrag(tq2, (32 * qb + run * KC) * RB2, cb);
         }
-        float cst[4][8];
-#pragma unroll
-        for (int which = 0; which < 4; ++which) {
+        auto row8 = [&](int which, float (&dst)[8]) __attribute__((always_inline)) {
           const float4* v = reinterpret_cast<const float4*>(&sVec(st)[which][32 * qb + 16 * run + 8 * half]);
           const float4 y0 = v[0], y1 = v[1];
-          cst[which][0] = y0.x; cst[which][1] = y0.y; cst[which][2] = y0.z; cst[which][3] = y0.w;
-          cst[which][4] = y1.x; cst[which][5] = y1.y; cst[which][6] = y1.z; cst[which][7] = y1.w;
-        }
+          dst[0] = y0.x; dst[1] = y0.y; dst[2] = y0.z; dst[3] = y0.w;
+          dst[4] = y1.x; dst[5] = y1.y; dst[6] = y1.z; dst[7] = y1.w;
+        };
+        float a1[8], a2[8], kl8[8];
+        row8(0, a1);
+        row8(1, a2);
+        row8(2, kl8);
         float ds1[8], ds2[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int r = 8 * run + i;
-          dS_both(s1[r], s2[r], c1, c2, cst[0][i], cst[1][i], cst[2][i], cst[2][i] * kLn2, cst[3][i], ds1[i],
-                  ds2[i]);
+          dS_both_abs(s1[r], s2[r], c1, c2, a1[i], a2[i], kl8[i], ds1[i], ds2[i]);
+        }
+        if (neg_tile) {
+          float sg[8];
+          row8(3, sg);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            ds1[i] *= sg[i];
+            ds2[i] *= sg[i];
+          }
         }
         if (need_mask) {
 #pragma unroll
@@ -352,15 +396,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_joint_dq_kernel(const BwdPara
   for (int c = 0; c < NC2; ++c)
     qf2[c] = qvalid ? M::load(q2p + (qi * p.sq2.n + c * KC + half * EPL) * ESZ) : M::zero();
 
-  float L1 = 0.f, L2 = 0.f, g = 0.f, gk = 0.f;
+  // Row constants of this lane's query row (see dS_both_abs); the sign of g
+  // multiplies the finished dQ rows.
+  float A1 = kZeroRow, A2 = kZeroRow, klr = 0.f;
   if (qvalid) {
     const int64_t o = bh * p.NQ + qi;
-    L1 = p.lse1[o] * kLog2e;
-    L2 = p.lse2[o] * kLog2e;
-    g = p.dkl[o];
-    gk = p.dkl[o] * p.kl[o];
+    joint_row_consts(p.lse1[o], p.lse2[o], p.dkl[o], A1, A2);
+    klr = p.kl[o];
   }
-  const float gl = g * kLn2;
 
   f32x16 dq1[NB1], dq2[NB2];
 #pragma unroll
@@ -436,7 +479,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_joint_dq_kernel(const BwdPara
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             const int r = 8 * run + i;
-            dS_both(s1[r], s2[r], c1, c2, L1, L2, g, gl, gk, ds1[i], ds2[i]);
+            dS_both_abs(s1[r], s2[r], c1, c2, A1, A2, klr, ds1[i], ds2[i]);
           }
           if (need_mask) {
 #pragma unroll
@@ -506,12 +549,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_joint_dq_kernel(const BwdPara
   for (int r = 0; r < 16; ++r) {
     const int64_t q = qw0 + acc_row(r, half);
     if (q < p.NQ) {
+      const bool neg = p.dkl[bh * p.NQ + q] < 0.f;
+      const float sc1 = neg ? -p.scale_g : p.scale_g, sc2 = neg ? -p.scale_s : p.scale_s;
 #pragma unroll
       for (int cb = 0; cb < NB1; ++cb)
-        *reinterpret_cast<T*>(dq1p + (q * p.sdq.n + 32 * cb + col) * ESZ) = from_f32<T>(dq1[cb][r] * p.scale_g);
+        *reinterpret_cast<T*>(dq1p + (q * p.sdq.n + 32 * cb + col) * ESZ) = from_f32<T>(dq1[cb][r] * sc1);
 #pragma unroll
       for (int cb = 0; cb < NB2; ++cb)
-        *reinterpret_cast<T*>(dq2p + (q * p.sdq_s.n + 32 * cb + col) * ESZ) = from_f32<T>(dq2[cb][r] * p.scale_s);
+        *reinterpret_cast<T*>(dq2p + (q * p.sdq_s.n + 32 * cb + col) * ESZ) = from_f32<T>(dq2[cb][r] * sc2);
     }
   }
 }

@@ -150,12 +150,12 @@ def test_underflowing_probabilities_stay_finite(gpu_lib, causal):
 
 
 @pytest.mark.parametrize("signs", ["mixed", "nonnegative"])
-@pytest.mark.parametrize("setting", ["student", "teacher"])
+@pytest.mark.parametrize("setting", ["student", "teacher", "joint"])
 def test_backward_zero_and_negative_row_gradients(gpu_lib, setting, signs):
     """Upstream gradients with exact zeros (every fifth row) and either mixed
-    signs or none negative: the dQ kernel folds log2 |g| into the exponents
-    (a zero g into an exponent that underflows) and applies the sign to the
-    finished dQ rows."""
+    signs or none negative: the kernels fold log2 |g| into the exponents (a
+    zero g into an exponent that underflows), apply the sign to the finished
+    dQ rows, and to dS in the dK tiles that have a row with g < 0."""
     w = W(f"gsign_{signs}", 1, 2, 300, 300, 128, 64, "bf16", True, synth.Recipe("iid", amp1=2.0))
     say(f"[row gradients {signs}] {setting}")
     x, t = to_device(w)
@@ -166,6 +166,18 @@ def test_backward_zero_and_negative_row_gradients(gpu_lib, setting, signs):
     x["g"] = g
     t["g"] = torch.from_numpy(g).cuda()
     _, (kl, l1, l2) = gpu_forward(gpu_lib, w, t)
+    if setting == "joint":
+        none = torch.empty(0, dtype=torch.float32, device="cuda")
+        dq1, dk1, dq2, dk2 = gpu_lib.skl_backward_joint(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, kl, t["g"],
+                                                        w.scale1, w.scale2, w.causal, ws=none)
+        torch.cuda.synchronize()
+        for st, dq, dk in (("teacher", dq1, dk1), ("student", dq2, dk2)):
+            rq, rk = oracle_backward(w, x, st)
+            dqn = grad_to_np(dq)
+            assert np.all(dqn[..., ::5, :] == 0.0), "rows with g = 0 must get dQ = 0 exactly"
+            check_grad(f"gsign joint dQ ({st}, {signs})", w, dqn, rq)
+            check_grad(f"gsign joint dK ({st}, {signs})", w, grad_to_np(dk), rk)
+        return
     if setting == "student":
         dq, dk = gpu_lib.skl_backward_student(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, t["g"],
                                               w.scale1, w.scale2, w.causal)
