@@ -397,8 +397,9 @@ def skl_recommended_splits(q1, k1, q2, k2, causal: bool = False, num_cus: Option
 # student call ("optimise P2") gives exactly dKL/d(Q2, K2) and the teacher
 # call ("optimise P1") exactly dKL/d(Q1, K1); backward launches only the
 # settings whose inputs require a gradient (a frozen teacher costs one).  When
-# both do, the two split calls run one after the other: on MI355X they are
-# faster than the joint kernels (algo="joint" selects those).
+# both do, the default ("auto") makes one joint call, which computes both
+# settings from one recompute and measures faster on MI355X than the two split
+# calls; algo="split" forces the two split calls.
 # ---------------------------------------------------------------------------
 
 def _autograd_function():
@@ -425,7 +426,7 @@ def _autograd_function():
             dq1 = dk1 = dq2 = dk2 = None
             need_s = ctx.needs_input_grad[2] or ctx.needs_input_grad[3]
             need_t = ctx.needs_input_grad[0] or ctx.needs_input_grad[1]
-            if algo == "joint":
+            if algo in ("joint", "auto"):
                 if need_s and need_t:
                     dq1, dk1, dq2, dk2 = skl_backward_joint(q1, k1, q2, k2, lse1, lse2, kl, g, scale1, scale2,
                                                             causal)
@@ -444,14 +445,17 @@ def _autograd_function():
 _ATTENTION_KL = None
 
 
-def attention_kl(q1, k1, q2, k2, scale1=None, scale2=None, causal: bool = False, algo="split"):
+def attention_kl(q1, k1, q2, k2, scale1=None, scale2=None, causal: bool = False, algo="auto"):
     """Differentiable per-row KL(P1 || P2), P_k = softmax(scale_k Q_k K_k^T).
 
     Returns (kl, lse1, lse2); kl [B, H, N_Q] fp32 carries gradients to every
     input that requires one (the LSEs are auxiliary and not differentiable).
-    Scales default to 1/sqrt(d_k).  algo: "split" (default; the measured
-    fastest), "fused_atomic", or "joint" (both settings from one recompute
-    when all four inputs need gradients)."""
+    Scales default to 1/sqrt(d_k).  algo: "auto" (default: the joint kernels
+    when both settings need gradients -- one recompute for both, the measured
+    fastest -- else the split kernels), "split", "fused_atomic", or "joint"
+    (the same as "auto")."""
+    if algo not in ("auto", "split", "fused_atomic", "joint"):
+        raise SklError(1, f"unknown backward algorithm {algo!r} (auto, split, fused_atomic, joint)")
     global _ATTENTION_KL
     if _ATTENTION_KL is None:
         _ATTENTION_KL = _autograd_function()

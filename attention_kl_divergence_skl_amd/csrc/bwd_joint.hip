@@ -175,8 +175,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_joint_dk_kernel(const BwdPara
   __syncthreads();
   const float c1 = p.c1, c2 = p.c2;
   const int prow = rperm(col);
-  const SwzAddr<RB1> ad1(prow, half, lane);
-  const SwzAddr<RB2> ad2(prow, half, lane);
 
   // One query step; the stage is a compile-time constant in the mask-free
   // steps (run in pairs), so it folds into the immediate offset of every
@@ -206,10 +204,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_joint_dk_kernel(const BwdPara
         // All operand fragments of the block are read before its MFMA chains
         // (one wave per SIMD: no other wave hides the LDS latency).
         frag pa1[NC1], pa2[NC2];
+        // (Per-chunk LDS offsets are left to the compiler, which keeps them as
+        // loop invariants; the stage folds into the immediate offset.)
+        const int qrow = 32 * qb + prow;
 #pragma unroll
-        for (int c = 0; c < NC1; ++c) pa1[c] = ad1.frag(tq1, 32 * qb * RB1, c);
+        for (int c = 0; c < NC1; ++c) pa1[c] = M::load(&tq1[T1::off(qrow, (c * KC + half * EPL) * ESZ)]);
 #pragma unroll
-        for (int c = 0; c < NC2; ++c) pa2[c] = ad2.frag(tq2, 32 * qb * RB2, c);
+        for (int c = 0; c < NC2; ++c) pa2[c] = M::load(&tq2[T2::off(qrow, (c * KC + half * EPL) * ESZ)]);
+        __builtin_amdgcn_sched_barrier(0);  // keep every read ahead of the MFMA chains
 #pragma unroll
         for (int c = 0; c < (NC1 > NC2 ? NC1 : NC2); ++c) {
           if (c < NC1) s1 = M::run(pa1[c], kf1[c], s1);
@@ -229,9 +231,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_joint_dk_kernel(const BwdPara
         frag bq1[NB1], bq2[NB2];
         if constexpr (EPL != 1) {
 #pragma unroll
-          for (int cb = 0; cb < NB1; ++cb) bq1[cb] = ad1.trfrag(tq1, (32 * qb + run * KC) * RB1, cb);
+          for (int cb = 0; cb < NB1; ++cb) bq1[cb] = lds_tr_frag_swz<RB1>(tq1, 32 * qb + run * KC, 32 * cb, lane);
 #pragma unroll
-          for (int cb = 0; cb < NB2; ++cb) bq2[cb] = ad2.trfrag(tq2, (32 * qb + run * KC) * RB2, cb);
+          for (int cb = 0; cb < NB2; ++cb) bq2[cb] = lds_tr_frag_swz<RB2>(tq2, 32 * qb + run * KC, 32 * cb, lane);
         }
         auto row8 = [&](int which, float (&dst)[8]) __attribute__((always_inline)) {
           const float4* v = reinterpret_cast<const float4*>(&sVec(st)[which][32 * qb + 16 * run + 8 * half]);
@@ -416,9 +418,29 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_joint_dq_kernel(const BwdPara
   const int64_t nsteps = kend > 0 ? (kend + BK - 1) / BK : 0;
   const int64_t wave_kmax = CAUSAL ? qw0 + 31 + off : p.NK - 1;
 
+  // A full key tile's direct-to-LDS loads take a wave-uniform base (scalar
+  // registers) plus one loop-invariant 32-bit lane offset per side (the
+  // swizzle repeats every 16 rows, so all of a wave's instructions share it);
+  // the ragged last tile takes the clamping loader.
+  const int64_t rs1 = p.sk1.n * ESZ, rs2 = p.sk2.n * ESZ;
+  constexpr int RPI1 = 1024 / RB1, RPI2 = 1024 / RB2;  // rows per load instruction
+  const int r01 = wave * RPI1 + lane / T1::CPR, r02 = wave * RPI2 + lane / T2::CPR;
+  const unsigned lo1 = (unsigned)(r01 * (int)rs1 + (((lane % T1::CPR) ^ T1::swz(r01)) * 16));
+  const unsigned lo2 = (unsigned)(r02 * (int)rs2 + (((lane % T2::CPR) ^ T2::swz(r02)) * 16));
   auto fetch = [&](int st, int64_t j0) {
-    tile_load_async<BK, RB1>(sK1(st), k1p, p.sk1.n * ESZ, (int)j0, (int)p.NK, wave, lane);
-    tile_load_async<BK, RB2>(sK2(st), k2p, p.sk2.n * ESZ, (int)j0, (int)p.NK, wave, lane);
+    if (j0 + BK <= p.NK) {
+      unsigned o1 = lo1, o2 = lo2;
+      asm volatile("" : "+v"(o1), "+v"(o2));  // keep the offsets 32-bit (see the forward kernel)
+#pragma unroll
+      for (int k = 0; k < BK / RPI1 / 4; ++k)
+        global_load_lds16(uniform_ptr(k1p + (j0 + 4 * k * RPI1) * rs1) + o1, sK1(st) + (wave + 4 * k) * 1024);
+#pragma unroll
+      for (int k = 0; k < BK / RPI2 / 4; ++k)
+        global_load_lds16(uniform_ptr(k2p + (j0 + 4 * k * RPI2) * rs2) + o2, sK2(st) + (wave + 4 * k) * 1024);
+    } else {
+      tile_load_async<BK, RB1>(sK1(st), k1p, rs1, (int)j0, (int)p.NK, wave, lane);
+      tile_load_async<BK, RB2>(sK2(st), k2p, rs2, (int)j0, (int)p.NK, wave, lane);
+    }
   };
 
   if (nsteps > 0) fetch(0, 0);
@@ -438,32 +460,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_joint_dq_kernel(const BwdPara
     if (!MASKED || wave_uniform(j0 <= wave_kmax)) {
       const bool need_mask =
           MASKED && wave_uniform((j0 + BK > p.NK) || (CAUSAL && j0 + BK - 1 > qw0 + off) || (qw0 + 32 > p.NQ));
-#pragma unroll
-      for (int kb = 0; kb < BK / 32; ++kb) {
-        f32x16 s1 = f32x16{}, s2 = f32x16{};
+      // Gradient work of block kb from its logit accumulators.
+      auto grad = [&](int kb, const f32x16& s1, const f32x16& s2) __attribute__((always_inline)) {
         const int klim = clamp_i32(p.NK - (j0 + kb * 32)), cmax = clamp_i32(qi + off - (j0 + kb * 32));
-        const int krow = kb * 32 + prow;
-        // All operand fragments of the block are read before its MFMA chains
-        // (one wave per SIMD: no other wave hides the LDS latency).
-        if constexpr (EPL != 1) {
-          frag ka1[NC1], ka2[NC2];
-#pragma unroll
-          for (int c = 0; c < NC1; ++c) ka1[c] = M::load(&tk1[T1::off(krow, (c * KC + half * EPL) * ESZ)]);
-#pragma unroll
-          for (int c = 0; c < NC2; ++c) ka2[c] = M::load(&tk2[T2::off(krow, (c * KC + half * EPL) * ESZ)]);
-#pragma unroll
-          for (int c = 0; c < (NC1 > NC2 ? NC1 : NC2); ++c) {
-            if (c < NC1) s1 = M::run(ka1[c], qf1[c], s1);
-            if (c < NC2) s2 = M::run(ka2[c], qf2[c], s2);
-          }
-        } else {
-#pragma unroll
-          for (int c = 0; c < NC1; ++c)
-            s1 = M::run(M::load(&tk1[T1::off(krow, (c * KC + half * EPL) * ESZ)]), qf1[c], s1);
-#pragma unroll
-          for (int c = 0; c < NC2; ++c)
-            s2 = M::run(M::load(&tk2[T2::off(krow, (c * KC + half * EPL) * ESZ)]), qf2[c], s2);
-        }
         // Registers 8 run .. 8 run + 7 hold keys kb 32 + 16 run + 8 half + 0..7.
 #pragma unroll
         for (int run = 0; run < 2; ++run) {
@@ -516,6 +515,52 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_joint_dq_kernel(const BwdPara
 #pragma unroll
             for (int cb = 0; cb < NB2; ++cb) dq2[cb] = M::run(a2, bk2[cb], dq2[cb]);
           }
+        }
+      };
+      static_assert(BK == 64, "the step pipeline below assumes two 32-key blocks per tile");
+      if constexpr (EPL != 1) {
+        // Software pipeline over the tile's two blocks: all operand fragments
+        // of a block are read before its MFMA chains (one wave per SIMD: no
+        // other wave hides the LDS latency), and block 1's reads are issued
+        // right after block 0's chains, so their latency hides behind block
+        // 0's dS work, with which block 1's MFMAs can then interleave.
+        auto read = [&](int kb, frag (&f1)[NC1], frag (&f2)[NC2]) __attribute__((always_inline)) {
+          const int krow = kb * 32 + prow;
+#pragma unroll
+          for (int c = 0; c < NC1; ++c) f1[c] = M::load(&tk1[T1::off(krow, (c * KC + half * EPL) * ESZ)]);
+#pragma unroll
+          for (int c = 0; c < NC2; ++c) f2[c] = M::load(&tk2[T2::off(krow, (c * KC + half * EPL) * ESZ)]);
+        };
+        auto chain = [&](const frag (&f1)[NC1], const frag (&f2)[NC2], f32x16& s1, f32x16& s2)
+            __attribute__((always_inline)) {
+#pragma unroll
+          for (int c = 0; c < (NC1 > NC2 ? NC1 : NC2); ++c) {
+            if (c < NC1) s1 = M::run(f1[c], qf1[c], s1);
+            if (c < NC2) s2 = M::run(f2[c], qf2[c], s2);
+          }
+        };
+        f32x16 s1a = f32x16{}, s2a = f32x16{}, s1b = f32x16{}, s2b = f32x16{};
+        frag fa1[NC1], fa2[NC2], fb1[NC1], fb2[NC2];
+        read(0, fa1, fa2);
+        __builtin_amdgcn_sched_barrier(0);
+        chain(fa1, fa2, s1a, s2a);
+        read(1, fb1, fb2);
+        __builtin_amdgcn_sched_barrier(0);
+        chain(fb1, fb2, s1b, s2b);
+        grad(0, s1a, s2a);
+        grad(1, s1b, s2b);
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < BK / 32; ++kb) {
+          f32x16 s1 = f32x16{}, s2 = f32x16{};
+          const int krow = kb * 32 + prow;
+#pragma unroll
+          for (int c = 0; c < NC1; ++c)
+            s1 = M::run(M::load(&tk1[T1::off(krow, (c * KC + half * EPL) * ESZ)]), qf1[c], s1);
+#pragma unroll
+          for (int c = 0; c < NC2; ++c)
+            s2 = M::run(M::load(&tk2[T2::off(krow, (c * KC + half * EPL) * ESZ)]), qf2[c], s2);
+          grad(kb, s1, s2);
         }
       }
     }

@@ -2,12 +2,15 @@
 """Benchmark of the fused attention-KL hot path on one MI355X.
 
 One step = one pass of the whole hot path over one batch of synthetic input
-already resident in HBM: skl_forward (one-pass forward), then
-skl_backward_student (optimise P2) and skl_backward_teacher (optimise P1),
-each a dK kernel and a dQ kernel (--bwd-algo joint: one skl_backward_joint
-call for both settings; fused_atomic: the fused kernel with its workspace
-clear and dQ convert).  W untimed warm-up steps, then
-exactly K timed steps between two device synchronisations.
+already resident in HBM: skl_forward (one-pass forward), then the gradients
+of both settings, optimise P2 (student) and optimise P1 (teacher).  By default
+they come from one skl_backward_joint call (a joint dK kernel and a joint dQ
+kernel that share each pair's logits and exponentials between the settings;
+the library's fastest way to compute all four gradients).  --bwd-algo split
+makes skl_backward_student and skl_backward_teacher calls instead, each a dK
+kernel and a dQ kernel; fused_atomic the fused kernel with its workspace
+clear and dQ convert.  W untimed warm-up steps, then exactly K timed steps
+between two device synchronisations.
 
 Prints ONE JSON line.  `value` is the step's algorithmic TFLOP/s
 (2*pairs*[(d1+d2) + (d1+3*d2) + (3*d1+d2)] per step / step time).  The
@@ -209,9 +212,10 @@ def main(argv=None) -> int:
                          "(default: as the workload defines it)")
     ap.add_argument("--phases", default="fwd,student,teacher",
                     help="comma list of fwd, student, teacher, joint (profiling aid; the default is the "
-                         "full step; --bwd-algo joint turns student,teacher into joint)")
-    ap.add_argument("--bwd-algo", default="split", choices=["split", "fused_atomic", "joint"],
-                    help="joint: both settings in one skl_backward_joint call")
+                         "full step; with --bwd-algo joint, the default, student and teacher become joint)")
+    ap.add_argument("--bwd-algo", default="joint", choices=["joint", "split", "fused_atomic"],
+                    help="joint (default): both settings in one skl_backward_joint call; split: the "
+                         "student and teacher calls")
     ap.add_argument("--cpu-sub", type=int, default=16384, help="side of the causal block the oracle times")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MiB",
@@ -247,8 +251,8 @@ def main(argv=None) -> int:
         w = w.with_(causal=args.mask == "causal")
     phases = [p for p in args.phases.split(",") if p]
     algo = args.bwd_algo
-    if algo == "joint":
-        phases = [p for p in phases if p not in ("student", "teacher")] + ["joint"]
+    if algo == "joint" and any(p in ("student", "teacher") for p in phases):
+        phases = [p for p in phases if p not in ("student", "teacher", "joint")] + ["joint"]
     for p in phases:
         if p not in ("fwd", "student", "teacher", "joint"):
             raise SystemExit(f"unknown phase {p}")

@@ -17,7 +17,7 @@ def W(name, B, H, NQ, NK, d1, d2, dtype, causal, recipe=synth.Recipe("corr", noi
                           recipe, "random", 3)
 
 
-@pytest.mark.parametrize("algo", ["split", "joint"])
+@pytest.mark.parametrize("algo", ["auto", "split", "joint"])
 @pytest.mark.parametrize("w", [W("ag_bf16_causal", 1, 2, 300, 300, 128, 128, "bf16", True),
                                W("ag_f32_noncausal", 2, 1, 130, 200, 64, 128, "f32", False, synth.Recipe("iid"))],
                          ids=lambda w: w.name)
