@@ -91,6 +91,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_joint_dk_kernel(const BwdPara
   // some row of the tile has g < 0.
   __shared__ __attribute__((aligned(16))) float sVa[4][BQ], sVb[4][BQ];
   __shared__ int sNeg[2];
+
   auto sQ1 = [&](int st) __attribute__((always_inline)) -> char* { return st ? sQ1b : sQ1a; };
   auto sQ2 = [&](int st) __attribute__((always_inline)) -> char* { return st ? sQ2b : sQ2a; };
   auto sVec = [&](int st) __attribute__((always_inline)) -> float(*)[BQ] { return st ? sVb : sVa; };
@@ -187,41 +188,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_joint_dk_kernel(const BwdPara
     const char* const tq1 = sQ1(st);
     const char* const tq2 = sQ2(st);
     const bool neg_tile = __builtin_amdgcn_readfirstlane(sNeg[st]) != 0;
-#pragma unroll
-    for (int qb = 0; qb < BQ / 32; ++qb) {
+    // Gradient work of query block qb from its logit accumulators.
+    // Registers 8 run .. 8 run + 7 hold rows 32 qb + 16 run + 8 half + 0..7
+    // (the rperm order): they form K chunk `run` (bf16) or chunks
+    // 8 run .. 8 run + 7 (fp32) of both dK products.
+    auto grad = [&](int qb, const f32x16& s1, const f32x16& s2) __attribute__((always_inline)) {
       const int64_t qb0 = q0 + 32 * qb;
-      if (MASKED && (kw0 >= p.NK || qb0 >= p.NQ || (CAUSAL && kw0 > qb0 + 31 + off))) continue;  // fully masked
-      f32x16 s1 = f32x16{}, s2 = f32x16{};
-      if constexpr (EPL == 1) {
-        const int qrow = 32 * qb + prow;
-#pragma unroll
-        for (int c = 0; c < NC1; ++c)
-          s1 = M::run(M::load(&tq1[T1::off(qrow, (c * KC + half * EPL) * ESZ)]), kf1[c], s1);
-#pragma unroll
-        for (int c = 0; c < NC2; ++c)
-          s2 = M::run(M::load(&tq2[T2::off(qrow, (c * KC + half * EPL) * ESZ)]), kf2[c], s2);
-      } else {
-        // All operand fragments of the block are read before its MFMA chains
-        // (one wave per SIMD: no other wave hides the LDS latency).
-        frag pa1[NC1], pa2[NC2];
-        // (Per-chunk LDS offsets are left to the compiler, which keeps them as
-        // loop invariants; the stage folds into the immediate offset.)
-        const int qrow = 32 * qb + prow;
-#pragma unroll
-        for (int c = 0; c < NC1; ++c) pa1[c] = M::load(&tq1[T1::off(qrow, (c * KC + half * EPL) * ESZ)]);
-#pragma unroll
-        for (int c = 0; c < NC2; ++c) pa2[c] = M::load(&tq2[T2::off(qrow, (c * KC + half * EPL) * ESZ)]);
-        __builtin_amdgcn_sched_barrier(0);  // keep every read ahead of the MFMA chains
-#pragma unroll
-        for (int c = 0; c < (NC1 > NC2 ? NC1 : NC2); ++c) {
-          if (c < NC1) s1 = M::run(pa1[c], kf1[c], s1);
-          if (c < NC2) s2 = M::run(pa2[c], kf2[c], s2);
-        }
-      }
-
-      // Registers 8 run .. 8 run + 7 hold rows 32 qb + 16 run + 8 half + 0..7
-      // (the rperm order): they form K chunk `run` (bf16) or chunks
-      // 8 run .. 8 run + 7 (fp32) of both dK products.
       const bool need_mask = MASKED && ((qb0 + 32 > p.NQ) || (kw0 + 32 > p.NK) || (CAUSAL && kw0 + 31 > qb0 + off));
       const int qlim = clamp_i32(p.NQ - qb0), cmin = clamp_i32(key - qb0 - off);
 #pragma unroll
@@ -284,17 +256,75 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_joint_dk_kernel(const BwdPara
                                dk2[cb]);
           }
         } else {
-          frag a1, a2;
+          frag a1f, a2f;
 #pragma unroll
           for (int e = 0; e < EPL; ++e) {
-            a1[e] = from_f32<T>(ds1[e]);
-            a2[e] = from_f32<T>(ds2[e]);
+            a1f[e] = from_f32<T>(ds1[e]);
+            a2f[e] = from_f32<T>(ds2[e]);
           }
 #pragma unroll
-          for (int cb = 0; cb < NB1; ++cb) dk1[cb] = M::run(a1, bq1[cb], dk1[cb]);
+          for (int cb = 0; cb < NB1; ++cb) dk1[cb] = M::run(a1f, bq1[cb], dk1[cb]);
 #pragma unroll
-          for (int cb = 0; cb < NB2; ++cb) dk2[cb] = M::run(a2, bq2[cb], dk2[cb]);
+          for (int cb = 0; cb < NB2; ++cb) dk2[cb] = M::run(a2f, bq2[cb], dk2[cb]);
         }
+      }
+    };
+    // Logits of query block qb.  bf16: all operand fragments are read before
+    // the MFMA chains (one wave per SIMD: no other wave hides the LDS
+    // latency); per-chunk LDS offsets are left to the compiler, which keeps
+    // them as loop invariants (the stage folds into the immediate offset).
+    auto read = [&](int qb, frag (&f1)[NC1], frag (&f2)[NC2]) __attribute__((always_inline)) {
+      const int qrow = 32 * qb + prow;
+#pragma unroll
+      for (int c = 0; c < NC1; ++c) f1[c] = M::load(&tq1[T1::off(qrow, (c * KC + half * EPL) * ESZ)]);
+#pragma unroll
+      for (int c = 0; c < NC2; ++c) f2[c] = M::load(&tq2[T2::off(qrow, (c * KC + half * EPL) * ESZ)]);
+    };
+    auto chain = [&](const frag (&f1)[NC1], const frag (&f2)[NC2], f32x16& s1, f32x16& s2)
+        __attribute__((always_inline)) {
+#pragma unroll
+      for (int c = 0; c < (NC1 > NC2 ? NC1 : NC2); ++c) {
+        if (c < NC1) s1 = M::run(f1[c], kf1[c], s1);
+        if (c < NC2) s2 = M::run(f2[c], kf2[c], s2);
+      }
+    };
+    static_assert(BQ == 64, "the step pipeline below assumes two 32-row query blocks per tile");
+    if constexpr (EPL != 1 && !MASKED) {
+      // Mask-free step, software-pipelined over its two query blocks: block
+      // 1's reads are issued right after block 0's MFMA chains, so their
+      // latency hides behind block 0's dS work, with which block 1's MFMAs
+      // can then interleave.
+      f32x16 s1a = f32x16{}, s2a = f32x16{}, s1b = f32x16{}, s2b = f32x16{};
+      frag fa1[NC1], fa2[NC2], fb1[NC1], fb2[NC2];
+      read(0, fa1, fa2);
+      __builtin_amdgcn_sched_barrier(0);
+      chain(fa1, fa2, s1a, s2a);
+      read(1, fb1, fb2);
+      __builtin_amdgcn_sched_barrier(0);
+      chain(fb1, fb2, s1b, s2b);
+      grad(0, s1a, s2a);
+      grad(1, s1b, s2b);
+    } else {
+#pragma unroll
+      for (int qb = 0; qb < BQ / 32; ++qb) {
+        const int64_t qb0 = q0 + 32 * qb;
+        if (MASKED && (kw0 >= p.NK || qb0 >= p.NQ || (CAUSAL && kw0 > qb0 + 31 + off))) continue;  // fully masked
+        f32x16 s1 = f32x16{}, s2 = f32x16{};
+        if constexpr (EPL == 1) {
+          const int qrow = 32 * qb + prow;
+#pragma unroll
+          for (int c = 0; c < NC1; ++c)
+            s1 = M::run(M::load(&tq1[T1::off(qrow, (c * KC + half * EPL) * ESZ)]), kf1[c], s1);
+#pragma unroll
+          for (int c = 0; c < NC2; ++c)
+            s2 = M::run(M::load(&tq2[T2::off(qrow, (c * KC + half * EPL) * ESZ)]), kf2[c], s2);
+        } else {
+          frag f1[NC1], f2[NC2];
+          read(qb, f1, f2);
+          __builtin_amdgcn_sched_barrier(0);  // keep every read ahead of the MFMA chains
+          chain(f1, f2, s1, s2);
+        }
+        grad(qb, s1, s2);
       }
     }
     if (it + 1 < nsteps) stash(st ^ 1, q0 + BQ);
