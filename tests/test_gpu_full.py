@@ -1,5 +1,6 @@
 """GPU parity at the full evaluation sizes, through the same entry points
-bench.py times.  The oracle checks sampled rows exactly (each row's KL, LSE
+bench.py times (the forward, the joint backward call it times by default, and
+the student and teacher calls of its split mode).  The oracle checks sampled rows exactly (each row's KL, LSE
 and dQ only need that row), sampled key columns near the end of causal
 sequences (few rows see them), whole heads at 16K (every row and key column
 of dQ and dK), the first key columns at 64K (every query row sees them, so the
@@ -98,6 +99,33 @@ def check_sampled_backward(w, dq, dk, setting, early_cols_head=None):
     assert torch.isfinite(dq_np).all() and torch.isfinite(dk_np).all()
 
 
+def backward_calls(gpu_lib, t, w, kl, l1, l2, causal):
+    """(setting, dq, dk) for the student call, the teacher call and both
+    settings of one joint call, one call at a time (each frees before the next)."""
+    for call in ("student", "teacher", "joint"):
+        say(f"[full] {w.name} {call} backward causal={causal}")
+        if call == "student":
+            dq, dk = gpu_lib.skl_backward_student(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, t["g"],
+                                                  w.scale1, w.scale2, causal)
+            torch.cuda.synchronize()
+            yield "student", dq, dk
+            del dq, dk
+        elif call == "teacher":
+            dq, dk = gpu_lib.skl_backward_teacher(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, kl, t["g"],
+                                                  w.scale1, w.scale2, causal)
+            torch.cuda.synchronize()
+            yield "teacher", dq, dk
+            del dq, dk
+        else:
+            dq1, dk1, dq2, dk2 = gpu_lib.skl_backward_joint(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, kl, t["g"],
+                                                            w.scale1, w.scale2, causal)
+            torch.cuda.synchronize()
+            yield "teacher", dq1, dk1
+            del dq1, dk1
+            yield "student", dq2, dk2
+            del dq2, dk2
+
+
 def test_causal_4k_all_settings(gpu_lib, store):
     w, t = inputs(store, "causal_4k_h8x2_d128_corr03")
     say("[full] causal 4K forward + both backward settings")
@@ -143,32 +171,25 @@ def test_16k_forward_and_splitk(gpu_lib, store, causal):
 
 @pytest.mark.parametrize("causal", [True, False])
 def test_16k_backward_full_head(gpu_lib, store, causal):
-    """Both backward settings at 16K x 16K, 32 heads: every row of dQ and every
-    key column of dK of one head against the oracle (early key columns walk
-    every query tile, late ones only the diagonal), sampled rows of two more
-    heads, and sum_j dK_j = 0 for all heads."""
+    """Both backward settings at 16K x 16K, 32 heads, through the student and
+    teacher calls and through one joint call: every row of dQ and every key
+    column of dK of one head against the oracle (early key columns walk every
+    query tile, late ones only the diagonal), sampled rows of two more heads,
+    and sum_j dK_j = 0 for all heads."""
     w0, t = inputs(store, "n16k_h32_d128_corr05")
     w = w0.with_(causal=causal)
     kl, l1, l2 = gpu_lib.skl_forward(t["q1"], t["k1"], t["q2"], t["k2"], w.scale1, w.scale2, causal)
     b, h = 0, w.H - 1
     q1, k1, q2, k2 = synth.head_inputs(w, b, h)
     g = synth.head_grad(w, b, h)
-    for setting in ("student", "teacher"):
-        say(f"[full] 16K {setting} backward causal={causal}")
-        if setting == "student":
-            dq, dk = gpu_lib.skl_backward_student(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, t["g"],
-                                                  w.scale1, w.scale2, causal)
-        else:
-            dq, dk = gpu_lib.skl_backward_teacher(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, kl, t["g"],
-                                                  w.scale1, w.scale2, causal)
-        torch.cuda.synchronize()
-        rq, rk = oracle.head_backward(q1, k1, q2, k2, w.scale1, w.scale2, causal, g, setting)
+    ref = {s_: oracle.head_backward(q1, k1, q2, k2, w.scale1, w.scale2, causal, g, s_) for s_ in ("student", "teacher")}
+    for setting, dq, dk in backward_calls(gpu_lib, t, w, kl, l1, l2, causal):
+        rq, rk = ref[setting]
         check_grad(f"16K ({b},{h}) dQ {setting} causal={causal}", w, dq[b, h].float().cpu().numpy(), rq,
                    per_head_axis=False)
         check_grad(f"16K ({b},{h}) dK {setting} causal={causal}", w, dk[b, h].float().cpu().numpy(), rk,
                    per_head_axis=False)
         check_sampled_backward(w, dq, dk, setting)
-        del dq, dk
 
 
 def test_causal_64k_forward_student_teacher(gpu_lib, store):
@@ -190,6 +211,22 @@ def test_causal_64k_forward_student_teacher(gpu_lib, store):
     check_sampled_backward(w, dq, dk, "teacher", early_cols_head=(0, 5))
 
 
+def test_causal_64k_joint_backward(gpu_lib, store):
+    """The joint call bench.py times by default, at its full size: sampled
+    rows and trailing key columns of both settings, the first key columns of
+    one head (teacher; the two dK products share the kernel's loop), and
+    sum_j dK_j = 0 for every head."""
+    w, t = inputs(store, "causal_64k_h32_d128_q1x4")
+    kl, l1, l2 = gpu_lib.skl_forward(t["q1"], t["k1"], t["q2"], t["k2"], w.scale1, w.scale2, True)
+    say("[full] causal 64K joint backward")
+    dq1, dk1, dq2, dk2 = gpu_lib.skl_backward_joint(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, kl, t["g"],
+                                                    w.scale1, w.scale2, True)
+    torch.cuda.synchronize()
+    check_sampled_backward(w, dq1, dk1, "teacher", early_cols_head=(0, 9))
+    del dq1, dk1
+    check_sampled_backward(w, dq2, dk2, "student")
+
+
 def test_causal_128k_indexer_student(gpu_lib, store):
     w, t = inputs(store, "causal_128k_h8_d128_d64")
     say("[full] causal 128K (d1=128, d2=64) forward")
@@ -201,6 +238,13 @@ def test_causal_128k_indexer_student(gpu_lib, store):
                                           w.scale1, w.scale2, True)
     torch.cuda.synchronize()
     check_sampled_backward(w, dq, dk, "student")
+    del dq, dk
+    say("[full] causal 128K joint backward")
+    dq1, dk1, dq2, dk2 = gpu_lib.skl_backward_joint(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, kl, t["g"],
+                                                    w.scale1, w.scale2, True)
+    torch.cuda.synchronize()
+    check_sampled_backward(w, dq1, dk1, "teacher")
+    check_sampled_backward(w, dq2, dk2, "student")
 
 
 @pytest.mark.parametrize("name", ["causal_256k_h4_d128", "causal_512k_h2_d128"])
@@ -212,17 +256,8 @@ def test_long_context_forward_and_both_backward(gpu_lib, store, name):
     kl, l1, l2 = gpu_lib.skl_forward(t["q1"], t["k1"], t["q2"], t["k2"], w.scale1, w.scale2, True)
     torch.cuda.synchronize()
     check_sampled_forward(w, kl, l1, l2)
-    for setting in ("student", "teacher"):
-        say(f"[full] {name} {setting} backward")
-        if setting == "student":
-            dq, dk = gpu_lib.skl_backward_student(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, t["g"],
-                                                  w.scale1, w.scale2, True)
-        else:
-            dq, dk = gpu_lib.skl_backward_teacher(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, kl, t["g"],
-                                                  w.scale1, w.scale2, True)
-        torch.cuda.synchronize()
+    for setting, dq, dk in backward_calls(gpu_lib, t, w, kl, l1, l2, True):
         check_sampled_backward(w, dq, dk, setting)
-        del dq, dk
 
 
 def test_query_chunk_of_long_sequence(gpu_lib, store):
