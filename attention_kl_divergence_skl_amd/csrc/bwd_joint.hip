@@ -16,12 +16,16 @@
 //
 // The two sets of gradient accumulators (128 fp32 registers per lane at
 // d = 128) do not fit two waves per SIMD, so these kernels run one wave per
-// SIMD with the accumulators in the accumulation registers.  Per matrix
-// instruction they need about one exponential and four other vector ops,
-// a mix a single wave can hide behind its MFMAs when the instruction stream
-// interleaves the two; as compiled (matrix phase, then vector phase, per
-// block) they run at about the speed of the two settings one after the
-// other.  The tile layout, operand orders and masking follow bwd_split.hip.
+// SIMD with the accumulators in the accumulation registers.  With no second
+// wave to hide latency, each wave hides its own: every operand fragment of
+// a block is read before its MFMA chains, the gradient operands before the
+// dS work, and the mask-free steps run their two 32-row (32-key) blocks as a
+// software pipeline (block 1's reads issued right after block 0's MFMA
+// chains, so they land during block 0's dS work).  Doing about two thirds of
+// the instructions of the two settings run one after the other, the kernels
+// also run at a higher clock under the chip's power limit, and the joint
+// call takes about 0.8x the time of the two split calls.  The tile layout,
+// operand orders and masking follow bwd_split.hip.
 
 #include <type_traits>
 

@@ -52,13 +52,30 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def code_text(path: str) -> str:
+    """A source file's code without its comments, whitespace collapsed: an
+    edit to comments or layout leaves the hash (and so the recorded counter
+    figures) valid.  C-family files lose // and /* */ comments (the kernel
+    sources have no string literal containing them), Python files their
+    full-line # comments."""
+    import re
+
+    with open(path, encoding="utf-8") as fh:
+        text = fh.read()
+    if path.endswith(".py"):
+        text = "\n".join(ln for ln in text.splitlines() if not ln.lstrip().startswith("#"))
+    else:
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_sha(kernel: str) -> str:
     h = hashlib.sha256()
     pkg = os.path.join(ROOT, "attention_kl_divergence_skl_amd")
     # the build script carries per-source compiler flags, so it is hashed too
     for path in [os.path.join(pkg, "csrc", f) for f in KERNEL_SOURCES[kernel]] + [os.path.join(pkg, "build.py")]:
-        with open(path, "rb") as fh:
-            h.update(fh.read())
+        h.update(code_text(path).encode())
     return h.hexdigest()[:16]
 
 

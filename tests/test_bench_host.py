@@ -72,3 +72,19 @@ def test_kernel_bytes_and_hbm_report():
     assert abs(r["hbm_gbs"] - 800.0) < 1e-9 and abs(r["traffic_ratio"] - 4.0) < 1e-12
     assert abs(r["hbm_frac"] - 0.1) < 1e-12
     assert bench.hbm_report(10, None, 1.0)["hbm_gbs"] is None
+
+
+def test_code_hash_ignores_comments_but_not_code(tmp_path):
+    """The counter figures are keyed to a hash of the kernel code: comments
+    and layout do not change it, code does."""
+    a = tmp_path / "a.hip"
+    a.write_text("// header\nint f(int x) {  /* note */ return x + 1; }  // tail\n")
+    b = tmp_path / "b.hip"
+    b.write_text("int f(int x)\n{\n  return x + 1;\n}\n")
+    c = tmp_path / "c.hip"
+    c.write_text("int f(int x) { return x + 2; }\n")
+    assert bench.code_text(str(a)) == bench.code_text(str(b))
+    assert bench.code_text(str(a)) != bench.code_text(str(c))
+    p = tmp_path / "b.py"
+    p.write_text("# comment\nFLAGS = ['-O3']  # kept: code\n")
+    assert bench.code_text(str(p)) == "FLAGS = ['-O3'] # kept: code"
