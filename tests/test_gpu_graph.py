@@ -1,9 +1,9 @@
 """The entry points in a captured graph (torch.cuda.CUDAGraph on the HIP
-stream): forward, split-K forward + reduce and both backward settings are
-captured once and replayed several times, with eager work and
-synchronisations in between; every replay must equal the eager results
-bitwise (all of these kernels are deterministic, and the calls clear nothing
-with memset and allocate nothing themselves)."""
+stream): forward, split-K forward + reduce, both backward settings and the
+joint backward call are captured once and replayed several times, with eager
+work and synchronisations in between; every replay must equal the eager
+results bitwise (all of these kernels are deterministic, and the calls clear
+nothing with memset and allocate nothing themselves)."""
 import numpy as np
 import pytest
 import torch
@@ -17,12 +17,13 @@ pytestmark = pytest.mark.gpu
 def test_graph_replays_match_eager(gpu_lib):
     w = synth.Workload("graph", 1, 2, 300, 420, 128, 128, "bf16", True, 1 / np.sqrt(128), 1 / np.sqrt(128),
                        synth.Recipe("corr", noise=0.4), "random", 77)
-    say("[graph] capture forward, split-K, both backward settings")
+    say("[graph] capture forward, split-K, both backward settings, joint backward")
     _, t = to_device(w)
     q1, k1, q2, k2, g = t["q1"], t["k1"], t["q2"], t["k2"], t["g"]
     splits = 3
     ws_bytes = gpu_lib.skl_forward_splitk_workspace_size(q1, k1, q2, k2, splits)
     ws = torch.empty(ws_bytes // 4, dtype=torch.float32, device="cuda")
+    none = torch.empty(0, dtype=torch.float32, device="cuda")
 
     def run():
         kl, l1, l2 = gpu_lib.skl_forward(q1, k1, q2, k2, w.scale1, w.scale2, True)
@@ -30,7 +31,8 @@ def test_graph_replays_match_eager(gpu_lib):
         skl_kl, s1, s2 = gpu_lib.skl_reduce(ws, splits, w.B, w.H, w.NQ)
         dq2, dk2 = gpu_lib.skl_backward_student(q1, k1, q2, k2, l1, l2, g, w.scale1, w.scale2, True)
         dq1, dk1 = gpu_lib.skl_backward_teacher(q1, k1, q2, k2, l1, l2, kl, g, w.scale1, w.scale2, True)
-        return [kl, l1, l2, skl_kl, s1, s2, dq2, dk2, dq1, dk1]
+        joint = gpu_lib.skl_backward_joint(q1, k1, q2, k2, l1, l2, kl, g, w.scale1, w.scale2, True, ws=none)
+        return [kl, l1, l2, skl_kl, s1, s2, dq2, dk2, dq1, dk1, *joint]
 
     eager = [x.clone() for x in run()]
     torch.cuda.synchronize()

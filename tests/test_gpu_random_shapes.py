@@ -1,8 +1,9 @@
-"""A fixed, seeded sweep of random small shapes through the forward and both
-backward settings against the oracle.  The kernels decide per step whether
-masking is needed (causal diagonal, ragged query and key edges) and, with
-few query tiles, split the dQ kernel's keys into ranges; random N_Q, N_K,
-head dims, recipes and dtypes exercise those decisions together."""
+"""A fixed, seeded sweep of random small shapes through the forward, both
+backward settings (student and teacher calls) and the joint backward call
+against the oracle.  The kernels decide per step whether masking is needed
+(causal diagonal, ragged query and key edges) and, with few query tiles,
+split the dQ kernel's keys into ranges; random N_Q, N_K, head dims, recipes
+and dtypes exercise those decisions together."""
 import numpy as np
 import pytest
 import torch
@@ -41,8 +42,13 @@ def test_random_shape(gpu_lib, w):
                                             w.scale1, w.scale2, w.causal)
     dq1, dk1 = gpu_lib.skl_backward_teacher(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, kl, t["g"],
                                             w.scale1, w.scale2, w.causal)
+    none = torch.empty(0, dtype=torch.float32, device="cuda")  # no workspace: the joint kernels themselves
+    jq1, jk1, jq2, jk2 = gpu_lib.skl_backward_joint(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, kl, t["g"],
+                                                    w.scale1, w.scale2, w.causal, ws=none)
     torch.cuda.synchronize()
-    for setting, dq, dk in (("student", dq2, dk2), ("teacher", dq1, dk1)):
+    for setting, dq, dk, jq, jk in (("student", dq2, dk2, jq2, jk2), ("teacher", dq1, dk1, jq1, jk1)):
         rq, rk = oracle_backward(w, x, setting)
         check_grad(f"{w.name} dQ ({setting})", w, grad_to_np(dq), rq)
         check_grad(f"{w.name} dK ({setting})", w, grad_to_np(dk), rk)
+        check_grad(f"{w.name} joint dQ ({setting})", w, grad_to_np(jq), rq)
+        check_grad(f"{w.name} joint dK ({setting})", w, grad_to_np(jk), rk)
