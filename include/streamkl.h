@@ -220,7 +220,9 @@ skl_status skl_backward_teacher(const skl_shape* shape,
  * recompute-based tile-by-tile gradients").  With the student's and the
  * teacher's calls together this is the gradient of sum_i dkl_i KL_i with
  * respect to all four inputs.  Kernels: a joint dK kernel and a joint dQ
- * kernel (no atomics, bitwise deterministic).  ws is optional:
+ * kernel (no atomics, bitwise deterministic); when both settings need
+ * gradients this is the faster route (on MI355X about 0.8x the time of the
+ * student and teacher calls at 64K tokens).  ws is optional:
  * skl_backward_joint_workspace_size(shape) is nonzero only when the query
  * tiles alone cannot fill the device, and given that many bytes (16-byte
  * aligned) the call runs the two SKL_BWD_SPLIT settings one after the other
