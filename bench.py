@@ -366,12 +366,16 @@ def main(argv=None) -> int:
         call_ms = float(np.mean([a.elapsed_time(b) for a, b in pev[p]]))
         ks = {}
         for i, (name, fl) in enumerate(kflops[p].items()):
-            kms = float(np.mean([e[i].elapsed_time(e[i + 1]) for e in kev[p]]))
+            times = [e[i].elapsed_time(e[i + 1]) for e in kev[p]]
+            kms = float(np.mean(times))
             tf = fl / (kms * 1e-3) / 1e12
             atf = kalg[p][name] / (kms * 1e-3) / 1e12
             # tflops / pct_mfma_peak: the kernel's own MFMA work (matrix-core use);
-            # alg_tflops / pct_peak_alg: its share of the algorithmic count.
-            ks[name] = {"ms": kms, "tflops": tf, "pct_mfma_peak": 100.0 * tf / peak_tf,
+            # alg_tflops / pct_peak_alg: its share of the algorithmic count (both
+            # from the mean time; the min and median over the timed launches
+            # are reported beside it).
+            ks[name] = {"ms": kms, "ms_min": float(np.min(times)), "ms_median": float(np.median(times)),
+                        "tflops": tf, "pct_mfma_peak": 100.0 * tf / peak_tf,
                         "alg_tflops": atf, "pct_peak_alg": 100.0 * atf / peak_tf}
             # HBM: compulsory bytes, and the calibrated counter bytes of the
             # committed summary when it was taken on the current source.
