@@ -242,7 +242,7 @@ def main(argv=None) -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the attention-KL kernels here run on a single MI355X "
-              "(multi-GPU sharding is a design note, not part of this build); use --gpus 1.",
+              "(sharding across GPUs is described, not implemented); use --gpus 1.",
               file=sys.stderr, flush=True)
         return 2
 
