@@ -90,11 +90,25 @@ def test_strided_bnhd_layout(gpu_lib):
     check_rows(w.name, w, got, oracle_forward(w, x))
     dq, dk = gpu_lib.skl_backward_student(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, t["g"],
                                           w.scale1, w.scale2, w.causal)
+    dq1, dk1 = gpu_lib.skl_backward_teacher(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, kl, t["g"],
+                                            w.scale1, w.scale2, w.causal)
+    none = torch.empty(0, dtype=torch.float32, device="cuda")
+    joint = gpu_lib.skl_backward_joint(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, kl, t["g"],
+                                       w.scale1, w.scale2, w.causal, ws=none)
     torch.cuda.synchronize()
     assert dq.stride() == t["q2"].stride() and dk.stride() == t["k2"].stride()
+    for got_, ref_ in zip(joint, (t["q1"], t["k1"], t["q2"], t["k2"])):
+        assert got_.stride() == ref_.stride()
     rq, rk = oracle_backward(w, x, "student")
     check_grad("bnhd dQ2", w, grad_to_np(dq), rq)
     check_grad("bnhd dK2", w, grad_to_np(dk), rk)
+    check_grad("bnhd joint dQ2", w, grad_to_np(joint[2]), rq)
+    check_grad("bnhd joint dK2", w, grad_to_np(joint[3]), rk)
+    rq, rk = oracle_backward(w, x, "teacher")
+    check_grad("bnhd dQ1", w, grad_to_np(dq1), rq)
+    check_grad("bnhd dK1", w, grad_to_np(dk1), rk)
+    check_grad("bnhd joint dQ1", w, grad_to_np(joint[0]), rq)
+    check_grad("bnhd joint dK1", w, grad_to_np(joint[1]), rk)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
