@@ -18,8 +18,10 @@ Prints ONE JSON line.  `value` is the step's algorithmic TFLOP/s
 timed with HIP events recorded by the library itself around that kernel on
 its launch stream: `achieved` is its share of the algorithmic flops (logits a
 split backward kernel recomputes count half) over its mean launch time, and
-`mfma_work_tflops` the rate of all the MFMA work it issues; `cpu_baseline` is the float64 CPU oracle timed on a
-bounded causal sub-problem of the same workload.
+`mfma_work_tflops` the rate of all the MFMA work it issues; `noncausal` times
+the same calls on the same inputs without the causal mask; `cpu_baseline` is
+the float64 CPU oracle timed on a bounded causal sub-problem of the same
+workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
 """
@@ -218,6 +220,62 @@ def kernel_alg_bytes(w, phase: str, algo: str):
     return {"bwd_fused_kernel": inputs + rv + BH * (w.NQ + w.NK) * dg * e}
 
 
+def other_mask_leg(skl, torch, np, w, t, phases, algo, ws_s, ws_t, peak_tf, steps: int):
+    """The same inputs and calls without the causal mask (twice the pairs):
+    one untimed step, then `steps` timed ones; each call timed with events
+    around it on the current stream."""
+    from attention_kl_divergence_skl_amd import workmodel
+
+    wn = w.with_(causal=False)
+    wk = workmodel.work(wn.B, wn.H, wn.NQ, wn.NK, wn.d1, wn.d2, False, 2 if wn.dtype == "bf16" else 4)
+    alg = {"fwd": wk.fwd_flops, "student": wk.student_flops, "teacher": wk.teacher_flops,
+           "joint": wk.student_flops + wk.teacher_flops}
+    q1, k1, q2, k2, g = t["q1"], t["k1"], t["q2"], t["k2"], t["g"]
+    ev = {p: [] for p in phases}
+
+    def one(record):
+        kl, l1, l2 = None, None, None
+        for p in ("fwd", "student", "teacher", "joint"):
+            if p not in phases:
+                continue
+            if record:
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                e[0].record()
+            if p == "fwd":
+                kl, l1, l2 = skl.skl_forward(q1, k1, q2, k2, wn.scale1, wn.scale2, False)
+            elif p == "joint":
+                skl.skl_backward_joint(q1, k1, q2, k2, l1, l2, kl, g, wn.scale1, wn.scale2, False, ws=ws_t)
+            elif p == "student":
+                skl.skl_backward_student(q1, k1, q2, k2, l1, l2, g, wn.scale1, wn.scale2, False, algo=algo, ws=ws_s)
+            else:
+                skl.skl_backward_teacher(q1, k1, q2, k2, l1, l2, kl, g, wn.scale1, wn.scale2, False,
+                                         algo=algo, ws=ws_t)
+            if record:
+                e[1].record()
+                ev[p].append(e)
+
+    one(False)
+    torch.cuda.synchronize()
+    log(f"no mask: untimed step done; timing {steps}")
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        one(True)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) / steps * 1e3
+    out = {"workload": f"{w.name} without the causal mask", "causal": False, "steps": steps,
+           "ms_per_step": ms_step}
+    step_flops = sum(alg[p] for p in phases)
+    out["tflops"] = step_flops / (ms_step * 1e-3) / 1e12
+    out["pct_peak"] = 100.0 * out["tflops"] / peak_tf
+    out["phases"] = {}
+    for p in phases:
+        ms = float(np.mean([a.elapsed_time(b) for a, b in ev[p]]))
+        tf = alg[p] / (ms * 1e-3) / 1e12
+        out["phases"][p] = {"call_ms": ms, "algorithmic_tflops": tf, "pct_peak": 100.0 * tf / peak_tf}
+    log(f"no mask: {ms_step:.1f} ms per step, {out['tflops']:.1f} TFLOP/s")
+    return out
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -233,6 +291,8 @@ def main(argv=None) -> int:
     ap.add_argument("--bwd-algo", default="joint", choices=["joint", "split", "fused_atomic"],
                     help="joint (default): both settings in one skl_backward_joint call; split: the "
                          "student and teacher calls")
+    ap.add_argument("--noncausal-steps", type=int, default=2,
+                    help="timed steps of the same inputs without the mask (reported beside the main line; 0: skip)")
     ap.add_argument("--cpu-sub", type=int, default=16384, help="side of the causal block the oracle times")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MiB",
@@ -423,6 +483,9 @@ def main(argv=None) -> int:
         },
         "cpu_baseline": None,
     }
+    if args.noncausal_steps > 0 and w.causal and "fwd" in phases:
+        res["noncausal"] = other_mask_leg(skl, torch, np, w, t, phases, algo, ws_s, ws_t, peak_tf,
+                                          args.noncausal_steps)
     if not args.no_cpu_baseline:
         log(f"timing the oracle on a {args.cpu_sub}x{args.cpu_sub} block")
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_sub)

@@ -88,3 +88,45 @@ def test_code_hash_ignores_comments_but_not_code(tmp_path):
     p = tmp_path / "b.py"
     p.write_text("# comment\nFLAGS = ['-O3']  # kept: code\n")
     assert bench.code_text(str(p)) == "FLAGS = ['-O3'] # kept: code"
+
+
+def test_unmasked_leg_times_each_call_and_counts_all_pairs():
+    """The unmasked leg of the bench line runs the same calls with causal
+    off and prices each call at the full N_Q x N_K pair count; stand-ins for
+    torch and the library record which calls ran and give every call 4 ms."""
+    import types
+
+    import numpy as np
+
+    calls = []
+
+    class Ev:
+        def record(self):
+            pass
+
+        def elapsed_time(self, other):
+            return 4.0
+
+    fake_torch = types.SimpleNamespace(cuda=types.SimpleNamespace(Event=lambda enable_timing: Ev(),
+                                                                  synchronize=lambda: None))
+
+    def fwd(*a):
+        calls.append(("fwd", a[-1]))
+        return "kl", "l1", "l2"
+
+    def joint(*a, ws=None):
+        calls.append(("joint", a[-1]))
+        assert a[4:7] == ("l1", "l2", "kl")
+
+    fake_skl = types.SimpleNamespace(skl_forward=fwd, skl_backward_joint=joint)
+    w = synth.WORKLOADS["causal_64k_h32_d128_q1x4"]
+    t = {k: k for k in ("q1", "k1", "q2", "k2", "g")}
+    out = bench.other_mask_leg(fake_skl, fake_torch, np, w, t, ["fwd", "joint"], "joint", None, None, 2500.0, 3)
+    assert calls == [("fwd", False), ("joint", False)] * 4  # one untimed step, three timed
+    pairs = w.B * w.H * w.NQ * w.NK
+    assert out["causal"] is False and out["steps"] == 3
+    f = out["phases"]["fwd"]
+    assert abs(f["algorithmic_tflops"] - 2 * pairs * (w.d1 + w.d2) / 4e-3 / 1e12) < 1e-6
+    j = out["phases"]["joint"]
+    assert abs(j["algorithmic_tflops"] - 2 * pairs * 4 * (w.d1 + w.d2) / 4e-3 / 1e12) < 1e-6
+    assert abs(j["pct_peak"] - 100 * j["algorithmic_tflops"] / 2500.0) < 1e-9
