@@ -140,7 +140,9 @@ def cpu_baseline(w, n_sub: int):
 
 
 def copy_calibration(nbytes: int, reps: int) -> None:
-    """A plain copy kernel of known size, for scaling HBM byte counters."""
+    """Kernels of known traffic, for scaling HBM byte counters: a plain copy
+    (reads and writes nbytes) and a sum reduction of the same buffer (reads
+    nbytes, writes a few bytes), each `reps` times."""
     import torch
 
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -149,7 +151,12 @@ def copy_calibration(nbytes: int, reps: int) -> None:
     for _ in range(reps):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps}), flush=True)
+    total = torch.empty((), dtype=torch.float32, device="cuda")
+    for _ in range(reps):
+        torch.sum(src, dim=0, out=total)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "sum_bytes_read": nbytes,
+                      "reps": reps}), flush=True)
 
 
 def kernel_flops(w, wk, phase: str, algo: str):
@@ -296,7 +303,7 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-sub", type=int, default=16384, help="side of the causal block the oracle times")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MiB",
-                    help="only run a plain copy of this many MiB (counter calibration) and exit")
+                    help="only run a plain copy and a sum reduction of this many MiB (counter calibration) and exit")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
