@@ -130,3 +130,45 @@ def test_unmasked_leg_times_each_call_and_counts_all_pairs():
     j = out["phases"]["joint"]
     assert abs(j["algorithmic_tflops"] - 2 * pairs * 4 * (w.d1 + w.d2) / 4e-3 / 1e12) < 1e-6
     assert abs(j["pct_peak"] - 100 * j["algorithmic_tflops"] / 2500.0) < 1e-9
+
+
+def test_unmasked_leg_with_split_calls_passes_algorithm_and_workspaces():
+    """With --bwd-algo split the leg makes the student and teacher calls,
+    each with the algorithm and its own workspace, after the forward."""
+    import types
+
+    import numpy as np
+
+    calls = []
+
+    class Ev:
+        def record(self):
+            pass
+
+        def elapsed_time(self, other):
+            return 2.0
+
+    fake_torch = types.SimpleNamespace(cuda=types.SimpleNamespace(Event=lambda enable_timing: Ev(),
+                                                                  synchronize=lambda: None))
+
+    def fwd(*a):
+        calls.append("fwd")
+        return "kl", "l1", "l2"
+
+    def student(*a, algo=None, ws=None):
+        assert a[4:7] == ("l1", "l2", "g") and a[-1] is False
+        calls.append(("student", algo, ws))
+
+    def teacher(*a, algo=None, ws=None):
+        assert a[4:8] == ("l1", "l2", "kl", "g") and a[-1] is False
+        calls.append(("teacher", algo, ws))
+
+    fake_skl = types.SimpleNamespace(skl_forward=fwd, skl_backward_student=student, skl_backward_teacher=teacher)
+    w = synth.WORKLOADS["causal_64k_h32_d128_q1x4"]
+    t = {k: k for k in ("q1", "k1", "q2", "k2", "g")}
+    out = bench.other_mask_leg(fake_skl, fake_torch, np, w, t, ["fwd", "student", "teacher"], "split", "ws_s", "ws_t",
+                               2500.0, 1)
+    assert calls == ["fwd", ("student", "split", "ws_s"), ("teacher", "split", "ws_t")] * 2
+    pairs = w.B * w.H * w.NQ * w.NK
+    s = out["phases"]["student"]
+    assert abs(s["algorithmic_tflops"] - 2 * pairs * (w.d1 + 3 * w.d2) / 2e-3 / 1e12) < 1e-6
