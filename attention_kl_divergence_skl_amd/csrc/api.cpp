@@ -97,6 +97,10 @@ skl_status check_shape(const skl_shape* s, bool need_nk) {
 
 bool empty(const skl_shape* s) { return s->B == 0 || s->H == 0 || s->NQ == 0; }
 
+// An empty problem whose key gradients still have rows: no query sees any
+// key, so a backward call writes zeros into dK.
+bool keys_without_queries(const skl_shape* s) { return s->B > 0 && s->H > 0 && s->NQ == 0 && s->NK > 0; }
+
 skl_status check_ptr(const void* p, const char* name, bool align16 = true) {
   if (!p) return fail(SKL_ERR_INVALID_ARGUMENT, "%s is NULL", name);
   if (align16 && (reinterpret_cast<uintptr_t>(p) & 15u) != 0)
@@ -370,19 +374,25 @@ static skl_status backward_common(const skl_shape* s, const void* q1, const void
                                   const float* lse2, const float* kl, const float* dkl, void* dq, void* dk,
                                   int algo, void* ws, size_t ws_bytes, bool teacher, hipStream_t stream) {
   SKL_TRY(check_inputs(s, q1, k1, q2, k2, scale1, scale2, causal));
-  if (empty(s)) return ok();
+  if (algo != SKL_BWD_SPLIT && algo != SKL_BWD_FUSED_ATOMIC)
+    return fail(SKL_ERR_INVALID_ARGUMENT, "unknown backward algorithm %d", algo);
+  const int64_t* sqg = teacher ? s->sq1 : s->sq2;
+  const int64_t* skg = teacher ? s->sk1 : s->sk2;
+  const int64_t dgd = teacher ? s->d1 : s->d2;
+  if (empty(s)) {
+    if (!keys_without_queries(s)) return ok();
+    SKL_TRY(check_ptr(dk, teacher ? "dk1" : "dk2"));
+    SKL_TRY(check_grad_layout(skg, s->B, s->H, s->NK, dgd, teacher ? "k1" : "k2"));
+    return from_hip(skl::launch_zero_rows(dk, strides(skg), s->B, s->H, s->NK, (int)dgd, s->dtype, stream),
+                    "dK zero launch");
+  }
   SKL_TRY(check_ptr(lse1, "lse1", false));
   SKL_TRY(check_ptr(lse2, "lse2", false));
   if (teacher) SKL_TRY(check_ptr(kl, "kl", false));
   SKL_TRY(check_ptr(dkl, "dkl", false));
   SKL_TRY(check_ptr(dq, teacher ? "dq1" : "dq2"));
   SKL_TRY(check_ptr(dk, teacher ? "dk1" : "dk2"));
-  if (algo != SKL_BWD_SPLIT && algo != SKL_BWD_FUSED_ATOMIC)
-    return fail(SKL_ERR_INVALID_ARGUMENT, "unknown backward algorithm %d", algo);
   const bool fused = algo == SKL_BWD_FUSED_ATOMIC;
-  const int64_t* sqg = teacher ? s->sq1 : s->sq2;
-  const int64_t* skg = teacher ? s->sk1 : s->sk2;
-  const int64_t dgd = teacher ? s->d1 : s->d2;
   SKL_TRY(check_grad_layout(sqg, s->B, s->H, s->NQ, dgd, teacher ? "q1" : "q2"));
   SKL_TRY(check_grad_layout(skg, s->B, s->H, s->NK, dgd, teacher ? "k1" : "k2"));
   SKL_TRY(check_grid(s->B * s->H * cdiv(s->NK, skl::kBwdBK), "backward (key tiles)"));
@@ -499,7 +509,16 @@ skl_status skl_backward_joint(const skl_shape* s, const void* q1, const void* k1
                               const float* kl, const float* dkl, void* dq1, void* dk1, void* dq2, void* dk2,
                               void* ws, size_t ws_bytes, hipStream_t stream) {
   SKL_TRY(check_inputs(s, q1, k1, q2, k2, scale1, scale2, causal));
-  if (empty(s)) return ok();
+  if (empty(s)) {
+    if (!keys_without_queries(s)) return ok();
+    SKL_TRY(check_ptr(dk1, "dk1"));
+    SKL_TRY(check_ptr(dk2, "dk2"));
+    SKL_TRY(check_grad_layout(s->sk1, s->B, s->H, s->NK, s->d1, "k1"));
+    SKL_TRY(check_grad_layout(s->sk2, s->B, s->H, s->NK, s->d2, "k2"));
+    hipError_t e = skl::launch_zero_rows(dk1, strides(s->sk1), s->B, s->H, s->NK, s->d1, s->dtype, stream);
+    if (e == hipSuccess) e = skl::launch_zero_rows(dk2, strides(s->sk2), s->B, s->H, s->NK, s->d2, s->dtype, stream);
+    return from_hip(e, "dK zero launch");
+  }
   SKL_TRY(check_ptr(lse1, "lse1", false));
   SKL_TRY(check_ptr(lse2, "lse2", false));
   SKL_TRY(check_ptr(kl, "kl", false));

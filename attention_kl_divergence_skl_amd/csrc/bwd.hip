@@ -261,6 +261,21 @@ __global__ __launch_bounds__(256) void zero_kernel(float4* __restrict__ ws, int6
     ws[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
+// Zeros into a strided [B, H, N, d] tensor with a contiguous d axis and
+// 16-byte aligned rows: the key gradient of a backward call with no query
+// rows, where no kernel above runs.
+__global__ __launch_bounds__(256) void zero_rows_kernel(char* __restrict__ base, const Strides st, int64_t H,
+                                                        int64_t N, int64_t rows, int chunks, int esz) {
+  const int64_t n = rows * chunks;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t row = i / chunks;
+    const int64_t bh = row / N, r = row % N;
+    const int64_t b = bh / H, h = bh % H;
+    float4* dst = reinterpret_cast<float4*>(base + (b * st.b + h * st.h + r * st.n) * esz) + (i % chunks);
+    *dst = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
 // ws fp32 [B*H][NQ][dg] -> dq (input dtype, caller strides) times scale.
 template <typename T>
 __global__ __launch_bounds__(256) void convert_kernel(const ConvertParams p) {
@@ -329,6 +344,16 @@ hipError_t launch_zero(float* ws, int64_t count, hipStream_t s) {
   const int64_t n4 = count / 4;  // count is a multiple of 64 (head dims 64 / 128)
   hipLaunchKernelGGL(zero_kernel, dim3((unsigned)grid_for(n4, 256)), dim3(256), 0, s,
                      reinterpret_cast<float4*>(ws), n4);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_rows(void* dst, const Strides& st, int64_t B, int64_t H, int64_t N, int d, int dtype,
+                            hipStream_t s) {
+  const int esz = dtype == 0 ? 2 : 4;
+  const int chunks = d * esz / 16;  // 16-byte pieces per row (head dims 64 / 128)
+  const int64_t rows = B * H * N;
+  hipLaunchKernelGGL(zero_rows_kernel, dim3((unsigned)grid_for(rows * chunks, 256)), dim3(256), 0, s,
+                     static_cast<char*>(dst), st, H, N, rows, chunks, esz);
   return hipGetLastError();
 }
 

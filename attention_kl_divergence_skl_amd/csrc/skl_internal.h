@@ -114,6 +114,9 @@ hipError_t launch_backward_split(const BwdParams& p, int dtype, int d1, int d2, 
 hipError_t launch_backward_joint(const BwdParams& p, int dtype, int d1, int d2, bool causal, int64_t BH,
                                  hipStream_t s, void (*between)(hipStream_t));
 hipError_t launch_convert(const ConvertParams& p, int dtype, hipStream_t s);
+// Zeros into a strided [B, H, N, d] tensor (16-byte aligned rows).
+hipError_t launch_zero_rows(void* dst, const Strides& st, int64_t B, int64_t H, int64_t N, int d, int dtype,
+                            hipStream_t s);
 
 // Records a printf-style message as this thread's last error (skl_last_error)
 // and returns `status` (api.cpp).

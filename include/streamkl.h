@@ -35,8 +35,11 @@
  * - Validation happens on the host before anything is enqueued; on any
  *   error nothing is enqueued and no output is touched.  A launch failure
  *   reported by the HIP runtime returns SKL_ERR_HIP.
- * - Sizes of zero (B, H or N_Q) are valid and enqueue nothing.  N_K = 0 with
- *   N_Q > 0 is invalid (an empty softmax).
+ * - Sizes of zero (B, H or N_Q) are valid and enqueue nothing, with one
+ *   exception: a backward call with N_Q = 0 < N_K (and B, H > 0) writes zeros
+ *   into its key gradients, which have rows although no query sees them (it
+ *   needs only their pointers; the other row and query pointers may be NULL).
+ *   N_K = 0 with N_Q > 0 is invalid (an empty softmax).
  * - N_Q and N_K must be below 2^30 and B * H at most 2^31 (row indices are
  *   32-bit inside the kernels); larger sizes return SKL_ERR_UNSUPPORTED.
  *   So does a shape whose kernels would need more than (2^32 - 1) / 256

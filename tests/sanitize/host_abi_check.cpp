@@ -247,6 +247,25 @@ static void backward_checks() {
   CHECK(stub::log.joint == 1 && stub::log.split == 2 && stub::log.convert == 2);
   CHECK(skl_backward_joint(&s, q1, k1, q2, k2, 0.1f, 0.1f, 0, o1, o2, nullptr, o4, g1, g2, g3, g4, nullptr, 0,
                            nullptr) == SKL_ERR_INVALID_ARGUMENT);
+
+  // No query rows but keys: every backward call writes zeros into its key
+  // gradients (and needs them), nothing else; no rows at all: nothing.
+  const skl_shape nq = shape(2, 3, 0, 77, 128, 64);
+  stub::log = {};
+  CHECK(student(nq) == SKL_OK);
+  CHECK(stub::log.zero_rows == 1 && stub::log.zero_rows_dst == g2 && stub::log.zero_rows_rows == 2 * 3 * 77 &&
+        stub::log.zero_rows_d == 64 && stub::log.split == 0);
+  CHECK(teacher(nq, SKL_BWD_FUSED_ATOMIC) == SKL_OK);
+  CHECK(stub::log.zero_rows == 2 && stub::log.zero_rows_dst == g2 && stub::log.zero_rows_d == 128 &&
+        stub::log.fused == 0 && stub::log.zero == 0);
+  CHECK(joint(nq) == SKL_OK);
+  CHECK(stub::log.zero_rows == 4 && stub::log.zero_rows_dst == g4 && stub::log.joint == 0);
+  CHECK(skl_backward_student(&nq, nullptr, nullptr, nullptr, nullptr, 0.1f, 0.1f, 0, nullptr, nullptr, nullptr,
+                             nullptr, nullptr, SKL_BWD_SPLIT, nullptr, 0, nullptr) == SKL_ERR_INVALID_ARGUMENT);
+  CHECK(student(nq, 7) == SKL_ERR_INVALID_ARGUMENT);  // unknown algorithm, also for an empty problem
+  stub::log = {};
+  CHECK(student(shape(0, 3, 0, 77)) == SKL_OK && joint(shape(2, 3, 0, 0)) == SKL_OK);
+  CHECK(stub::log.zero_rows == 0);
 }
 
 static void misc_checks() {

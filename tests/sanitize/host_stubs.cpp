@@ -77,6 +77,13 @@ hipError_t launch_backward_joint(const BwdParams& p, int, int, int, bool, int64_
   if (between) between(s);
   return hipSuccess;
 }
+hipError_t launch_zero_rows(void* dst, const Strides&, int64_t B, int64_t H, int64_t N, int d, int, hipStream_t) {
+  ++stub::log.zero_rows;
+  stub::log.zero_rows_dst = dst;
+  stub::log.zero_rows_rows = B * H * N;
+  stub::log.zero_rows_d = d;
+  return hipSuccess;
+}
 hipError_t launch_convert(const ConvertParams& p, int, hipStream_t) {
   ++stub::log.convert;
   stub::log.conv = p;

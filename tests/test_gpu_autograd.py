@@ -83,3 +83,20 @@ def test_autograd_key_broadcast_over_heads(gpu_lib):
         gpu_lib.skl_backward_teacher(t["q1"], k1.detach(), t["q2"], t["k2"], l1, l2, kl2, t["g"],
                                      w.scale1, w.scale2, True)
     assert e.value.status == 2
+
+
+def test_autograd_without_query_rows(gpu_lib):
+    """An empty query block: KL has no rows and every input gradient is
+    zero (the key gradients have rows and are written as zeros)."""
+    say("[autograd] no query rows")
+    g = torch.Generator(device="cpu").manual_seed(9)
+    k1 = torch.randn(1, 2, 40, 64, generator=g).to("cuda", torch.bfloat16).requires_grad_()
+    k2 = torch.randn(1, 2, 40, 64, generator=g).to("cuda", torch.bfloat16).requires_grad_()
+    q1 = torch.empty(1, 2, 0, 64, dtype=torch.bfloat16, device="cuda", requires_grad=True)
+    q2 = torch.empty(1, 2, 0, 64, dtype=torch.bfloat16, device="cuda", requires_grad=True)
+    kl, _, _ = gpu_lib.attention_kl(q1, k1, q2, k2, causal=True)
+    assert kl.shape == (1, 2, 0)
+    kl.sum().backward()
+    for t in (q1, k1, q2, k2):
+        assert t.grad is not None and t.grad.shape == t.shape
+        assert torch.equal(t.grad, torch.zeros_like(t.grad))

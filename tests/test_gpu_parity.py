@@ -416,3 +416,35 @@ def test_joint_backward_with_key_range_workspace(gpu_lib, w):
         rq, rk = oracle_backward(w, x, setting)
         check_grad(f"{w.name} joint dQ ({setting})", w, grad_to_np(dq), rq)
         check_grad(f"{w.name} joint dK ({setting})", w, grad_to_np(dk), rk)
+
+
+@pytest.mark.parametrize("call", ["student", "teacher", "joint", "fused_atomic"])
+def test_backward_without_query_rows_zeroes_key_gradients(gpu_lib, call):
+    """N_Q = 0 < N_K: no query sees any key, so every key gradient is exactly
+    zero and the call must write it (the outputs are fresh allocations; the
+    same-sized blocks are first filled with NaN and handed back to the
+    allocator, so memory left unwritten would show)."""
+    say(f"[no query rows] {call}")
+    B, H, NK, d1, d2 = 2, 3, 77, 128, 64
+    g = torch.Generator(device="cpu").manual_seed(5)
+    k1 = torch.randn(B, H, NK, d1, generator=g).to("cuda", torch.bfloat16)
+    k2 = torch.randn(B, H, NK, d2, generator=g).to("cuda", torch.bfloat16)
+    q1 = torch.empty(B, H, 0, d1, dtype=torch.bfloat16, device="cuda")
+    q2 = torch.empty(B, H, 0, d2, dtype=torch.bfloat16, device="cuda")
+    rows = [torch.empty(B, H, 0, dtype=torch.float32, device="cuda") for _ in range(4)]
+    for t in (k1, k2, k1, k2):
+        junk = torch.full_like(t, float("nan"))
+        del junk
+    if call == "student":
+        dks = [gpu_lib.skl_backward_student(q1, k1, q2, k2, rows[0], rows[1], rows[3], causal=True)[1]]
+    elif call == "teacher":
+        dks = [gpu_lib.skl_backward_teacher(q1, k1, q2, k2, *rows, causal=True)[1]]
+    elif call == "joint":
+        _, dk1, _, dk2 = gpu_lib.skl_backward_joint(q1, k1, q2, k2, *rows, causal=True)
+        dks = [dk1, dk2]
+    else:
+        dks = [gpu_lib.skl_backward_student(q1, k1, q2, k2, rows[0], rows[1], rows[3], algo="fused_atomic")[1],
+               gpu_lib.skl_backward_teacher(q1, k1, q2, k2, *rows, algo="fused_atomic")[1]]
+    torch.cuda.synchronize()
+    for dk in dks:
+        assert dk.shape[2] == NK and torch.equal(dk, torch.zeros_like(dk)), f"{call}: key gradient not zero"
