@@ -4,8 +4,9 @@ the student and teacher calls of its split mode).  The oracle checks sampled row
 and dQ only need that row), sampled key columns near the end of causal
 sequences (few rows see them), whole heads at 16K (every row and key column
 of dQ and dK), the first key columns at 64K (every query row sees them, so the
-dK kernel walks all query tiles for them), and, for every head, a property
-that holds at any size: the key gradients of a head sum to zero."""
+dK kernel walks all query tiles for them), and, for every head, properties
+that hold at any size: the key gradients of a head sum to zero, and
+sum_i <q_i, dQ_i> equals sum_j <k_j, dK_j> (both are scale * sum dS (q . k))."""
 import numpy as np
 import pytest
 import torch
@@ -97,6 +98,23 @@ def check_sampled_backward(w, dq, dk, setting, early_cols_head=None):
     f = dk.double().norm(dim=(2, 3))
     assert torch.all(s <= 1e-2 * f + 1e-30), f"{w.name}: key gradients do not sum to zero ({setting})"
     assert torch.isfinite(dq_np).all() and torch.isfinite(dk_np).all()
+
+
+def check_dq_dk_identity(w, q, k, dq, dk, setting):
+    """Property at any size, for every head: sum_i <q_i, dQ_i> and
+    sum_j <k_j, dK_j> of the optimised side are both scale * sum_ij dS_ij
+    (q_i . k_j), so they agree up to rounding (the two kernels recompute dS
+    separately and round it to bf16 on their own).  A dK tile that is missing,
+    wrongly scaled or given the wrong operand breaks the equality."""
+    a = (q.double() * dq.double()).sum(dim=(2, 3))
+    b = (k.double() * dk.double()).sum(dim=(2, 3))
+    mag = (q.double() * dq.double()).abs().sum(dim=(2, 3)) + (k.double() * dk.double()).abs().sum(dim=(2, 3))
+    err = ((a - b).abs() / mag).max().item()
+    tag = f"{w.name}{'' if w.causal else ' without the mask'} ({setting})"
+    say(f"[full] {tag}: sum <q, dQ> vs sum <k, dK>, worst head {err:.2e} of the term magnitude")
+    # Measured about 2e-6 at 64K; a missing key tile moves it by percents and a
+    # 1 % error in dK's scale by about 1e-3.
+    assert err <= 1e-4, f"{tag}: dQ / dK identity off by {err:.3e}"
 
 
 def backward_calls(gpu_lib, t, w, kl, l1, l2, causal):
@@ -223,8 +241,34 @@ def test_causal_64k_joint_backward(gpu_lib, store):
                                                     w.scale1, w.scale2, True)
     torch.cuda.synchronize()
     check_sampled_backward(w, dq1, dk1, "teacher", early_cols_head=(0, 9))
+    check_dq_dk_identity(w, t["q1"], t["k1"], dq1, dk1, "teacher")
     del dq1, dk1
     check_sampled_backward(w, dq2, dk2, "student")
+    check_dq_dk_identity(w, t["q2"], t["k2"], dq2, dk2, "student")
+
+
+def test_noncausal_64k_forward_and_joint_backward(gpu_lib, store):
+    """The same 64K x 64K inputs without the mask, as bench.py's unmasked leg
+    times them: the forward and the joint call on sampled rows, and for every
+    head sum_j dK_j = 0 and the dQ / dK identity.  (Key columns against the
+    oracle would need every row's full softmax: about ten minutes of the
+    oracle per head at this size, so the 16K whole-head test covers dK
+    columns without the mask.)"""
+    w, t = inputs(store, "causal_64k_h32_d128_q1x4")
+    wn = w.with_(causal=False)  # same seed, same tensors
+    say("[full] non-causal 64K forward")
+    kl, l1, l2 = gpu_lib.skl_forward(t["q1"], t["k1"], t["q2"], t["k2"], wn.scale1, wn.scale2, False)
+    torch.cuda.synchronize()
+    check_sampled_forward(wn, kl, l1, l2, rows_seed=3)
+    say("[full] non-causal 64K joint backward")
+    dq1, dk1, dq2, dk2 = gpu_lib.skl_backward_joint(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, kl, t["g"],
+                                                    wn.scale1, wn.scale2, False)
+    torch.cuda.synchronize()
+    check_sampled_backward(wn, dq1, dk1, "teacher")
+    check_dq_dk_identity(wn, t["q1"], t["k1"], dq1, dk1, "teacher")
+    del dq1, dk1
+    check_sampled_backward(wn, dq2, dk2, "student")
+    check_dq_dk_identity(wn, t["q2"], t["k2"], dq2, dk2, "student")
 
 
 def test_causal_128k_indexer_student(gpu_lib, store):
