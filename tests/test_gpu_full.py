@@ -58,10 +58,28 @@ def check_sampled_forward(w, kl, l1, l2, rows_seed=0):
             assert np.abs(got[k] - ref[k]).max() <= tol["lse"], f"{w.name} ({b},{h}) {k}"
 
 
-def check_sampled_backward(w, dq, dk, setting, early_cols_head=None):
+def check_dq_dk_identity(w, q, k, dq, dk, setting):
+    """Property at any size, for every head: sum_i <q_i, dQ_i> and
+    sum_j <k_j, dK_j> of the optimised side are both scale * sum_ij dS_ij
+    (q_i . k_j), so they agree up to rounding (the two kernels recompute dS
+    separately and round it to bf16 on their own).  A dK tile that is missing,
+    wrongly scaled or given the wrong operand breaks the equality."""
+    a = (q.double() * dq.double()).sum(dim=(2, 3))
+    b = (k.double() * dk.double()).sum(dim=(2, 3))
+    mag = (q.double() * dq.double()).abs().sum(dim=(2, 3)) + (k.double() * dk.double()).abs().sum(dim=(2, 3))
+    err = ((a - b).abs() / mag).max().item()
+    tag = f"{w.name}{'' if w.causal else ' without the mask'} ({setting})"
+    say(f"[full] {tag}: sum <q, dQ> vs sum <k, dK>, worst head {err:.2e} of the term magnitude")
+    # Measured about 2e-6 at 64K; a missing key tile moves it by percents and a
+    # 1 % error in dK's scale by about 1e-3.
+    assert err <= 1e-4, f"{tag}: dQ / dK identity off by {err:.3e}"
+
+
+def check_sampled_backward(w, dq, dk, setting, early_cols_head=None, t=None):
     """Sampled dQ rows and trailing dK columns of a few heads; with
     early_cols_head = (b, h), also key columns 0..31 of that head, which every
-    query row sees (the oracle materialises all rows for them)."""
+    query row sees (the oracle materialises all rows for them); with the
+    device inputs t, the dQ / dK identity for every head."""
     tol = TOL[w.dtype]["grad"]
     dq_np = dq.float()
     dk_np = dk.float()
@@ -93,28 +111,14 @@ def check_sampled_backward(w, dq, dk, setting, early_cols_head=None):
         assert e <= tol, f"{w.name} ({b},{h}) early dK ({setting}) rel L2 {e:.3e}"
         er = check_rows_grad(f"{w.name} ({b},{h}) early dK ({setting})", tol, got, rk)
         say(f"[full] early dK columns: rel L2 {e:.2e}, worst column {er:.2e}")
+    if t is not None:
+        side = "1" if setting == "teacher" else "2"
+        check_dq_dk_identity(w, t["q" + side], t["k" + side], dq, dk, setting)
     # Property at any size: sum_j dK[j] = 0 for every head.
     s = dk.double().sum(dim=2).norm(dim=-1)
     f = dk.double().norm(dim=(2, 3))
     assert torch.all(s <= 1e-2 * f + 1e-30), f"{w.name}: key gradients do not sum to zero ({setting})"
     assert torch.isfinite(dq_np).all() and torch.isfinite(dk_np).all()
-
-
-def check_dq_dk_identity(w, q, k, dq, dk, setting):
-    """Property at any size, for every head: sum_i <q_i, dQ_i> and
-    sum_j <k_j, dK_j> of the optimised side are both scale * sum_ij dS_ij
-    (q_i . k_j), so they agree up to rounding (the two kernels recompute dS
-    separately and round it to bf16 on their own).  A dK tile that is missing,
-    wrongly scaled or given the wrong operand breaks the equality."""
-    a = (q.double() * dq.double()).sum(dim=(2, 3))
-    b = (k.double() * dk.double()).sum(dim=(2, 3))
-    mag = (q.double() * dq.double()).abs().sum(dim=(2, 3)) + (k.double() * dk.double()).abs().sum(dim=(2, 3))
-    err = ((a - b).abs() / mag).max().item()
-    tag = f"{w.name}{'' if w.causal else ' without the mask'} ({setting})"
-    say(f"[full] {tag}: sum <q, dQ> vs sum <k, dK>, worst head {err:.2e} of the term magnitude")
-    # Measured about 2e-6 at 64K; a missing key tile moves it by percents and a
-    # 1 % error in dK's scale by about 1e-3.
-    assert err <= 1e-4, f"{tag}: dQ / dK identity off by {err:.3e}"
 
 
 def backward_calls(gpu_lib, t, w, kl, l1, l2, causal):
@@ -166,7 +170,8 @@ def test_causal_4k_all_settings(gpu_lib, store):
             rq, rk = oracle.head_backward(q1, k1, q2, k2, w.scale1, w.scale2, True, g, setting)
             check_grad(f"4K ({b},{h}) dQ {setting}", w, dq[b, h].float().cpu().numpy(), rq, per_head_axis=False)
             check_grad(f"4K ({b},{h}) dK {setting}", w, dk[b, h].float().cpu().numpy(), rk, per_head_axis=False)
-    check_sampled_backward(w, dq2, dk2, "student")
+    check_sampled_backward(w, dq2, dk2, "student", t=t)
+    check_sampled_backward(w, dq1, dk1, "teacher", t=t)
 
 
 @pytest.mark.parametrize("causal", [True, False])
@@ -207,7 +212,7 @@ def test_16k_backward_full_head(gpu_lib, store, causal):
                    per_head_axis=False)
         check_grad(f"16K ({b},{h}) dK {setting} causal={causal}", w, dk[b, h].float().cpu().numpy(), rk,
                    per_head_axis=False)
-        check_sampled_backward(w, dq, dk, setting)
+        check_sampled_backward(w, dq, dk, setting, t=t)
 
 
 def test_causal_64k_forward_student_teacher(gpu_lib, store):
@@ -220,13 +225,13 @@ def test_causal_64k_forward_student_teacher(gpu_lib, store):
     dq, dk = gpu_lib.skl_backward_student(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, t["g"],
                                           w.scale1, w.scale2, True)
     torch.cuda.synchronize()
-    check_sampled_backward(w, dq, dk, "student")
+    check_sampled_backward(w, dq, dk, "student", t=t)
     del dq, dk
     say("[full] causal 64K teacher backward")
     dq, dk = gpu_lib.skl_backward_teacher(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, kl, t["g"],
                                           w.scale1, w.scale2, True)
     torch.cuda.synchronize()
-    check_sampled_backward(w, dq, dk, "teacher", early_cols_head=(0, 5))
+    check_sampled_backward(w, dq, dk, "teacher", early_cols_head=(0, 5), t=t)
 
 
 def test_causal_64k_joint_backward(gpu_lib, store):
@@ -240,11 +245,9 @@ def test_causal_64k_joint_backward(gpu_lib, store):
     dq1, dk1, dq2, dk2 = gpu_lib.skl_backward_joint(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, kl, t["g"],
                                                     w.scale1, w.scale2, True)
     torch.cuda.synchronize()
-    check_sampled_backward(w, dq1, dk1, "teacher", early_cols_head=(0, 9))
-    check_dq_dk_identity(w, t["q1"], t["k1"], dq1, dk1, "teacher")
+    check_sampled_backward(w, dq1, dk1, "teacher", early_cols_head=(0, 9), t=t)
     del dq1, dk1
-    check_sampled_backward(w, dq2, dk2, "student")
-    check_dq_dk_identity(w, t["q2"], t["k2"], dq2, dk2, "student")
+    check_sampled_backward(w, dq2, dk2, "student", t=t)
 
 
 def test_noncausal_64k_forward_and_joint_backward(gpu_lib, store):
@@ -264,11 +267,9 @@ def test_noncausal_64k_forward_and_joint_backward(gpu_lib, store):
     dq1, dk1, dq2, dk2 = gpu_lib.skl_backward_joint(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, kl, t["g"],
                                                     wn.scale1, wn.scale2, False)
     torch.cuda.synchronize()
-    check_sampled_backward(wn, dq1, dk1, "teacher")
-    check_dq_dk_identity(wn, t["q1"], t["k1"], dq1, dk1, "teacher")
+    check_sampled_backward(wn, dq1, dk1, "teacher", t=t)
     del dq1, dk1
-    check_sampled_backward(wn, dq2, dk2, "student")
-    check_dq_dk_identity(wn, t["q2"], t["k2"], dq2, dk2, "student")
+    check_sampled_backward(wn, dq2, dk2, "student", t=t)
 
 
 def test_causal_128k_indexer_student(gpu_lib, store):
@@ -281,14 +282,14 @@ def test_causal_128k_indexer_student(gpu_lib, store):
     dq, dk = gpu_lib.skl_backward_student(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, t["g"],
                                           w.scale1, w.scale2, True)
     torch.cuda.synchronize()
-    check_sampled_backward(w, dq, dk, "student")
+    check_sampled_backward(w, dq, dk, "student", t=t)
     del dq, dk
     say("[full] causal 128K joint backward")
     dq1, dk1, dq2, dk2 = gpu_lib.skl_backward_joint(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, kl, t["g"],
                                                     w.scale1, w.scale2, True)
     torch.cuda.synchronize()
-    check_sampled_backward(w, dq1, dk1, "teacher")
-    check_sampled_backward(w, dq2, dk2, "student")
+    check_sampled_backward(w, dq1, dk1, "teacher", t=t)
+    check_sampled_backward(w, dq2, dk2, "student", t=t)
 
 
 @pytest.mark.parametrize("name", ["causal_256k_h4_d128", "causal_512k_h2_d128"])
@@ -301,7 +302,7 @@ def test_long_context_forward_and_both_backward(gpu_lib, store, name):
     torch.cuda.synchronize()
     check_sampled_forward(w, kl, l1, l2)
     for setting, dq, dk in backward_calls(gpu_lib, t, w, kl, l1, l2, True):
-        check_sampled_backward(w, dq, dk, setting)
+        check_sampled_backward(w, dq, dk, setting, t=t)
 
 
 def test_query_chunk_of_long_sequence(gpu_lib, store):
@@ -330,5 +331,5 @@ def test_query_chunk_of_long_sequence(gpu_lib, store):
             dq, dk = gpu_lib.skl_backward_teacher(t["q1"], t["k1"], t["q2"], t["k2"], l1, l2, kl, t["g"],
                                                   w.scale1, w.scale2, True)
         torch.cuda.synchronize()
-        check_sampled_backward(w, dq, dk, setting)
+        check_sampled_backward(w, dq, dk, setting, t=t)
         del dq, dk
